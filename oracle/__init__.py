@@ -1,0 +1,175 @@
+"""CPU oracle for the zero-computation-expert MoE forward (TEST INFRASTRUCTURE).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``oracle.c`` (plain fp32 C,
+built by :func:`build`) with numpy marshalling; it shares no code with the
+HIP library and never calls it.
+
+What it computes is documented, with the passages it follows, at the top of
+``oracle.c``: router logits, softmax over all N+Z experts, bias added for
+selection only, top-k with ties to the lower index, unbiased gates, SwiGLU
+FFN experts, zero experts as identity, and the combine
+``out = (sum of zero-slot gates) * x + sum_j gate_j * y_j``.
+
+Pins (tests/test_oracle_pins.py) tie each function to something other than
+itself: float64 library matmuls and softmax, brute-force top-k, the
+closed forms of all-zero routing, Z = 0 (textbook top-k softmax MoE) and
+identical experts, exact equivariance, and the model-size arithmetic printed
+on the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "_oracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+
+F32, BF16 = 0, 1
+_DT = {"f32": F32, "bf16": BF16}
+
+
+def build() -> str:
+    """Compile oracle.c into oracle/_oracle.so with gcc (always rebuilds)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC",
+           "-o", _SO + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_SO + ".tmp", _SO)
+    return _SO
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_router_logits.argtypes = [i64, i32, i32, vp, vp, i32, vp]
+        lib.oracle_route_from_logits.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp]
+        lib.oracle_counts.argtypes = [i64, i32, i32, vp, vp]
+        lib.oracle_token_output.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
+        lib.oracle_combine_given_routing.argtypes = [i64, i32, i32, i32, i32, vp, i32, vp, vp,
+                                                     vp, vp, vp, vp]
+        lib.oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, vp, vp, vp]
+        _lib = lib
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _storage(a: np.ndarray, dt: str) -> np.ndarray:
+    return _c(a, np.float32 if dt == "f32" else np.uint16)
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, dt: str) -> np.ndarray:
+    x, w = _storage(x, dt), _storage(w_router, dt)
+    T, d = x.shape
+    E = w.shape[0]
+    out = np.empty((T, E), dtype=np.float32)
+    _load().oracle_router_logits(T, d, E, _ptr(x), _ptr(w), _DT[dt], _ptr(out))
+    return out
+
+
+def route_from_logits(logits: np.ndarray, bias: np.ndarray, k: int):
+    """Returns idx [T,k] int32, gate [T,k] f32, margin [T] f32, probs [T,E] f32."""
+    logits = _c(logits, np.float32)
+    bias = _c(bias, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    gate = np.empty((T, k), dtype=np.float32)
+    margin = np.empty(T, dtype=np.float32)
+    probs = np.empty((T, E), dtype=np.float32)
+    _load().oracle_route_from_logits(T, E, k, _ptr(logits), _ptr(bias), _ptr(idx), _ptr(gate),
+                                     _ptr(margin), _ptr(probs))
+    return idx, gate, margin, probs
+
+
+def counts(idx: np.ndarray, E: int) -> np.ndarray:
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    out = np.empty(E, dtype=np.int32)
+    _load().oracle_counts(T, k, E, _ptr(idx), _ptr(out))
+    return out
+
+
+def token_output(x_row: np.ndarray, dt: str, N: int, idx_row, gate_row, experts: dict) -> np.ndarray:
+    """Output of one token; ``experts[e] = (W_gate[e], W_up[e], W_down[e])`` for
+    every FFN expert in ``idx_row`` (arrays in storage dtype)."""
+    x_row = _storage(x_row, dt)
+    d = x_row.shape[0]
+    idx_row = _c(idx_row, np.int32)
+    gate_row = _c(gate_row, np.float32)
+    k = idx_row.shape[0]
+    keep = []
+    pg = (ctypes.c_void_p * k)()
+    pu = (ctypes.c_void_p * k)()
+    pd = (ctypes.c_void_p * k)()
+    I = 1
+    for j in range(k):
+        e = int(idx_row[j])
+        if e < N:
+            g, u, dn = (_storage(a, dt) for a in experts[e])
+            keep += [g, u, dn]
+            I = g.shape[0]
+            pg[j], pu[j], pd[j] = g.ctypes.data, u.ctypes.data, dn.ctypes.data
+    out = np.empty(d, dtype=np.float32)
+    _load().oracle_token_output(d, I, N, k, _ptr(x_row), _DT[dt], _ptr(idx_row), _ptr(gate_row),
+                                pg, pu, pd, _ptr(out))
+    return out
+
+
+def combine_given_routing(x, dt, N, idx, gate, w_gate, w_up, w_down) -> np.ndarray:
+    x = _storage(x, dt)
+    T, d = x.shape
+    idx = _c(idx, np.int32)
+    gate = _c(gate, np.float32)
+    k = idx.shape[1]
+    if N > 0:
+        w_gate, w_up, w_down = (_storage(a, dt) for a in (w_gate, w_up, w_down))
+        I = w_gate.shape[1]
+    else:
+        w_gate = w_up = w_down = None
+        I = 1
+    out = np.empty((T, d), dtype=np.float32)
+    _load().oracle_combine_given_routing(T, d, I, N, k, _ptr(x), _DT[dt], _ptr(idx), _ptr(gate),
+                                         _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out))
+    return out
+
+
+def forward(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, k: int, dt: str):
+    """Whole forward. Returns dict(out, counts, idx, gate, margin)."""
+    x = _storage(x, dt)
+    w_router = _storage(w_router, dt)
+    bias = _c(bias, np.float32)
+    T, d = x.shape
+    E = N + Z
+    if N > 0:
+        w_gate, w_up, w_down = (_storage(a, dt) for a in (w_gate, w_up, w_down))
+        I = w_gate.shape[1]
+    else:
+        w_gate = w_up = w_down = None
+        I = 1
+    out = np.empty((T, d), dtype=np.float32)
+    cnt = np.empty(E, dtype=np.int32)
+    idx = np.empty((T, k), dtype=np.int32)
+    gate = np.empty((T, k), dtype=np.float32)
+    margin = np.empty(T, dtype=np.float32)
+    _load().oracle_forward(T, d, I, N, Z, k, _DT[dt], _ptr(x), _ptr(w_router), _ptr(bias),
+                           _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(cnt), _ptr(idx),
+                           _ptr(gate), _ptr(margin))
+    return {"out": out, "counts": cnt, "idx": idx, "gate": gate, "margin": margin}

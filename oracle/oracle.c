@@ -1,0 +1,222 @@
+/*
+ * oracle.c -- plain, slow CPU definition of the zero-computation-expert MoE
+ * forward.  TEST INFRASTRUCTURE ONLY: used by tests/, by the smoke check and
+ * by the benchmark's CPU-baseline leg, never by the GPU product path.  It
+ * shares no code, header or table with the HIP library.
+ *
+ * Sources (the pages that describe the method):
+ *   [LCF-arch]  LongCat-Flash technical-report summary (zhangjingwei.cn page),
+ *               section 2 "architecture", item 1 "zero-computation experts":
+ *               tokens pick among FFN experts and Z zero-computation experts;
+ *               a zero-computation expert only returns its input, at no
+ *               compute cost; an expert-specific bias, adjusted by a
+ *               controller, shifts the routing scores so the share of FFN vs
+ *               zero experts stays on target.
+ *   [LCF-cfg]   same page, section 2, model-configuration paragraph: 512 FFN
+ *               experts of width 2048 and 256 zero experts per layer, 12
+ *               experts per token, hidden size 6144.
+ *   [LCF-infra] same page, section 5 "training infrastructure", numerical
+ *               precision item: BF16 results are judged against a CPU FP32
+ *               ground truth.  The oracle therefore computes in fp32, with
+ *               bfloat16 inputs widened exactly.
+ *   [KOL]       cnouyi.fund thread summarising the same report: the zero
+ *               expert acts as a "sink" for easy tokens; balancing is an
+ *               aux-loss-free bias in the style of DeepSeek-V3.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - routing score = softmax over all N+Z router logits (fp32, max-shifted);
+ *   - the bias is added to the softmax probability and used for selection
+ *     only; the gate of a selected expert is its unbiased probability, with
+ *     no renormalisation and no scale;
+ *   - an FFN expert is SwiGLU with three matrices and no biases:
+ *       y = W_down (silu(W_gate x) * (W_up x)),  silu(z) = z / (1 + e^-z);
+ *   - top-k order: biased score descending, equal scores -> lower index;
+ *   - output = (sum of zero-slot gates) * x + sum_j gate_j * y_j, the FFN
+ *     terms added in ascending slot order.
+ *
+ * Every sum is a plain left-to-right fp32 sum in ascending index order.
+ * Build: gcc -O2 -fopenmp -ffp-contract=off (OpenMP only splits tokens).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+/* Exact widening of an element of an fp32 or bfloat16 array to fp32. */
+static float orc_ld(const void *p, int64_t i, int dt) {
+  if (dt == ORC_F32) return ((const float *)p)[i];
+  uint32_t b = (uint32_t)((const uint16_t *)p)[i] << 16;
+  float f;
+  memcpy(&f, &b, sizeof f);
+  return f;
+}
+
+/* Step 1 of [LCF-arch]: router logits l[t,e] = sum_i x[t,i] * W_router[e,i]. */
+void oracle_router_logits(int64_t T, int d, int E, const void *x, const void *w_router, int dt,
+                          float *logits) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) {
+      float acc = 0.0f;
+      for (int i = 0; i < d; ++i)
+        acc += orc_ld(x, t * (int64_t)d + i, dt) * orc_ld(w_router, (int64_t)e * d + i, dt);
+      logits[t * (int64_t)E + e] = acc;
+    }
+  }
+}
+
+/* Softmax of one token's logits over all E experts (FFN and zero together). */
+static void orc_softmax(int E, const float *l, float *p) {
+  float m = l[0];
+  for (int e = 1; e < E; ++e)
+    if (l[e] > m) m = l[e];
+  float sum = 0.0f;
+  for (int e = 0; e < E; ++e) sum += expf(l[e] - m);
+  for (int e = 0; e < E; ++e) p[e] = expf(l[e] - m) / sum;
+}
+
+/* Steps 1-2 of [LCF-arch] from given logits: p = softmax(l); s = p + bias;
+ * idx = the k experts of largest s (ties -> lower index), listed by s
+ * descending; gate_j = p[idx_j]; margin = s_(k) - s_(k+1) (+inf if k == E).
+ * probs (nullable) receives p. */
+void oracle_route_from_logits(int64_t T, int E, int k, const float *logits, const float *bias,
+                              int32_t *idx, float *gate, float *margin, float *probs) {
+#pragma omp parallel
+  {
+    float *p = (float *)malloc(sizeof(float) * (size_t)E);
+    float *s = (float *)malloc(sizeof(float) * (size_t)E);
+    unsigned char *taken = (unsigned char *)malloc((size_t)E);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      orc_softmax(E, logits + t * (int64_t)E, p);
+      for (int e = 0; e < E; ++e) {
+        s[e] = p[e] + bias[e];
+        taken[e] = 0;
+      }
+      float last = 0.0f;
+      /* selection by repeated argmax: strictly greater wins, so the lowest
+       * index wins among equal scores */
+      for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+          if (!taken[e] && (best < 0 || s[e] > s[best])) best = e;
+        taken[best] = 1;
+        idx[t * k + j] = best;
+        gate[t * k + j] = p[best];
+        last = s[best];
+      }
+      if (margin) {
+        if (k >= E) {
+          margin[t] = INFINITY;
+        } else {
+          int nxt = -1;
+          for (int e = 0; e < E; ++e)
+            if (!taken[e] && (nxt < 0 || s[e] > s[nxt])) nxt = e;
+          margin[t] = last - s[nxt];
+        }
+      }
+      if (probs) memcpy(probs + t * (int64_t)E, p, sizeof(float) * (size_t)E);
+    }
+    free(p);
+    free(s);
+    free(taken);
+  }
+}
+
+/* Per-expert selection counts over all E experts ([LCF-arch], the quantity
+ * the bias controller consumes). */
+void oracle_counts(int64_t T, int k, int E, const int32_t *idx, int32_t *counts) {
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j) counts[idx[t * k + j]] += 1;
+}
+
+/* One SwiGLU FFN expert on one token: y = Wd (silu(Wg x) * (Wu x)).
+ * wg, wu: [I, d]; wd: [d, I]; h: scratch of I floats. */
+static void orc_expert(int d, int I, const float *x, const void *wg, const void *wu,
+                       const void *wd, int dt, float *h, float *y) {
+  for (int r = 0; r < I; ++r) {
+    float g = 0.0f, u = 0.0f;
+    for (int c = 0; c < d; ++c) {
+      g += orc_ld(wg, (int64_t)r * d + c, dt) * x[c];
+      u += orc_ld(wu, (int64_t)r * d + c, dt) * x[c];
+    }
+    h[r] = (g / (1.0f + expf(-g))) * u;
+  }
+  for (int i = 0; i < d; ++i) {
+    float acc = 0.0f;
+    for (int r = 0; r < I; ++r) acc += orc_ld(wd, (int64_t)i * I + r, dt) * h[r];
+    y[i] = acc;
+  }
+}
+
+/* Steps 3-5 of [LCF-arch] for one token with given routing: zero-expert slots
+ * (idx >= N) add gate * x (identity expert); FFN slots add gate * FFN(x).
+ * wg[j], wu[j], wd[j] point at the matrices of the expert in slot j (unused
+ * for zero slots).  out: d floats, in fp32. */
+void oracle_token_output(int d, int I, int N, int k, const void *x_row, int dt,
+                         const int32_t *idx, const float *gate, const void *const *wg,
+                         const void *const *wu, const void *const *wd, float *out) {
+  float *xf = (float *)malloc(sizeof(float) * (size_t)d);
+  float *y = (float *)malloc(sizeof(float) * (size_t)d);
+  float *h = (float *)malloc(sizeof(float) * (size_t)(I > 0 ? I : 1));
+  for (int i = 0; i < d; ++i) xf[i] = orc_ld(x_row, i, dt);
+  float zsum = 0.0f;
+  for (int j = 0; j < k; ++j)
+    if (idx[j] >= N) zsum += gate[j];
+  for (int i = 0; i < d; ++i) out[i] = zsum * xf[i];
+  for (int j = 0; j < k; ++j) {
+    if (idx[j] >= N) continue;
+    orc_expert(d, I, xf, wg[j], wu[j], wd[j], dt, h, y);
+    for (int i = 0; i < d; ++i) out[i] += gate[j] * y[i];
+  }
+  free(xf);
+  free(y);
+  free(h);
+}
+
+/* Steps 3-5 for tokens [0, T) given their routing; full weight tensors
+ * w_gate/w_up [N, I, d], w_down [N, d, I]. */
+void oracle_combine_given_routing(int64_t T, int d, int I, int N, int k, const void *x, int dt,
+                                  const int32_t *idx, const float *gate, const void *w_gate,
+                                  const void *w_up, const void *w_down, float *out) {
+  size_t es = dt == ORC_F32 ? 4 : 2;
+  size_t per = (size_t)I * (size_t)d * es;
+#pragma omp parallel
+  {
+    const void **pg = (const void **)malloc(sizeof(void *) * (size_t)k);
+    const void **pu = (const void **)malloc(sizeof(void *) * (size_t)k);
+    const void **pd = (const void **)malloc(sizeof(void *) * (size_t)k);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      for (int j = 0; j < k; ++j) {
+        int e = idx[t * k + j];
+        int ffn = e < N;
+        pg[j] = ffn ? (const char *)w_gate + (size_t)e * per : NULL;
+        pu[j] = ffn ? (const char *)w_up + (size_t)e * per : NULL;
+        pd[j] = ffn ? (const char *)w_down + (size_t)e * per : NULL;
+      }
+      oracle_token_output(d, I, N, k, (const char *)x + (size_t)t * (size_t)d * es, dt,
+                          idx + t * k, gate + t * k, pg, pu, pd, out + t * (int64_t)d);
+    }
+    free(pg);
+    free(pu);
+    free(pd);
+  }
+}
+
+/* The whole forward: logits, routing, counts and output (fp32). */
+void oracle_forward(int64_t T, int d, int I, int N, int Z, int k, int dt, const void *x,
+                    const void *w_router, const float *bias, const void *w_gate,
+                    const void *w_up, const void *w_down, float *out, int32_t *counts,
+                    int32_t *idx, float *gate, float *margin) {
+  int E = N + Z;
+  float *logits = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * (size_t)E);
+  oracle_router_logits(T, d, E, x, w_router, dt, logits);
+  oracle_route_from_logits(T, E, k, logits, bias, idx, gate, margin, NULL);
+  oracle_counts(T, k, E, idx, counts);
+  oracle_combine_given_routing(T, d, I, N, k, x, dt, idx, gate, w_gate, w_up, w_down, out);
+  free(logits);
+}
