@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the zero-computation-expert MoE forward on one MI355X.
+
+One step = one moe_zc_forward call (router, top-k, dispatch, the two expert
+GEMMs, combine) over one batch of synthetic tokens already resident in HBM.
+Default workload: the production-shaped prefill layer (T=8192 tokens,
+d=6144, 512 SwiGLU experts of width 2048, 256 zero experts, top-12, bf16).
+
+Prints ONE JSON line with tokens/s, the per-stage times measured with HIP
+events on the launch stream over the timed region, the roofline of the
+dominant kernel and the CPU oracle's throughput on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 1 MI355X; % bf16 MFMA peak (prefill) / % HBM BW (decode)"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prod", choices=["prod", "decode", "small", "skewed", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: auto)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, counts):
+    """Algorithmic FLOPs and HBM bytes of one step, and of each expert GEMM."""
+    import numpy as np
+
+    s = 2 if cfg.dtype == "bf16" else 4
+    cnt = np.asarray(counts, dtype=np.int64)
+    P = int(cnt[: cfg.N].sum())
+    touched = int((cnt[: cfg.N] > 0).sum())
+    T, d, I, E, k = cfg.T, cfg.d, cfg.I, cfg.E, cfg.k
+    per_expert = d * I * s
+    step_bytes = (T * d * s * 2 + E * d * s + touched * 3 * per_expert + E * 8 + T * k * 8)
+    step_flops = 6 * d * I * P + 2 * d * E * T
+    gate_up = {"bytes": touched * 2 * per_expert + T * d * s, "flops": 4 * d * I * P}
+    down = {"bytes": touched * per_expert, "flops": 2 * d * I * P}
+    router = {"bytes": T * d * s + E * d * s, "flops": 2 * d * E * T}
+    return {"P": P, "touched": touched, "step_bytes": step_bytes, "step_flops": step_flops,
+            "gate_up": gate_up, "down": down, "router": router}
+
+
+def cpu_baseline(cfg, dinp, ntok):
+    """The oracle, as it is, on the first `ntok` tokens of the same workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from tests import _parity as P
+
+    t0 = time.time()
+    x = synth.host_x(cfg, 0, ntok)
+    wr = synth.host_router(cfg)
+    bias = synth.host_bias(cfg)
+    w = {n: P.to_np(dinp["W_" + n]) for n in ("gate", "up", "down")}  # generator's device copy
+    prep = time.time() - t0
+    t1 = time.time()
+    oracle.forward(x, wr, bias, w["gate"], w["up"], w["down"], cfg.N, cfg.Z, cfg.k, cfg.dtype)
+    dt = time.time() - t1
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {ntok} of {cfg.T} tokens of the same workload (whole forward: "
+                      f"router, top-k, experts, combine); {dt:.1f}s of oracle time, "
+                      f"{prep:.1f}s input prep excluded"}
+
+
+def calibrate_copy():
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is "
+              "single-GPU by design and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import numpy as np
+    import torch
+
+    import synth
+    import zero_computation_expert_amd as moe
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    cfg = synth.CONFIGS[args.workload]
+    dev = "cuda:0"
+    t0 = time.time()
+    inp = synth.device_inputs(cfg, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for {cfg.name} generated on device in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    dt_code = moe.BF16 if cfg.dtype == "bf16" else moe.F32
+    nbytes = moe.workspace_bytes(cfg.T, cfg.d, cfg.I, cfg.N, cfg.Z, cfg.k, dt_code)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp["x"])
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    args_fwd = (inp["x"], inp["W_router"], inp["bias"], inp["W_gate"], inp["W_up"], inp["W_down"],
+                cfg.N, cfg.Z, cfg.k)
+    kw = dict(out=out, counts=counts, topk_idx=idx, topk_gate=gate, workspace=ws)
+
+    for _ in range(args.warmup):
+        moe.forward(*args_fwd, **kw)
+    torch.cuda.synchronize()
+    timer = moe.Timer(max(1, args.steps))
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        moe.forward(*args_fwd, **kw, timer=timer)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    ncalls, stage_ms = timer.read()
+    timer.close()
+    ms = total_ms / args.steps
+    stage_avg = {k: v / ncalls for k, v in stage_ms.items()}
+    print(f"[bench] {args.steps} steps: {ms:.3f} ms/step; stages " +
+          " ".join(f"{k}={v:.3f}" for k, v in stage_avg.items()), file=sys.stderr, flush=True)
+
+    alg = algorithmic(cfg, counts.cpu().numpy())
+    gu_s = stage_avg["gate_up"] / 1e3
+    dn_s = stage_avg["down"] / 1e3
+    rt_s = stage_avg["router"] / 1e3
+    peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    gu_gbs = alg["gate_up"]["bytes"] / gu_s / 1e9
+    roofline = {"bound": "hbm", "kernel": "gemm_kernel<bf16,GATE_UP> (gate/up GEMM + SwiGLU)",
+                "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": alg["gate_up"]["bytes"],
+                "avg_launch_ms": round(stage_avg["gate_up"], 4)}
+    kernels = {}
+    for name, sec in (("router", rt_s), ("gate_up", gu_s), ("down", dn_s)):
+        a = alg[name]
+        kernels[name] = {"ms": round(sec * 1e3, 4),
+                         "GB/s": round(a["bytes"] / sec / 1e9, 1),
+                         "TFLOP/s": round(a["flops"] / sec / 1e12, 1),
+                         "hbm_frac": round(a["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4),
+                         "mfma_frac": round(a["flops"] / sec / 1e12 / peak_tf, 4)}
+    step_s = ms / 1e3
+    res = {
+        "metric": METRIC,
+        "value": round(cfg.T / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Philox4x64 normals; random-init weights)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} I={cfg.I} N={cfg.N} Z={cfg.Z} "
+                               f"k={cfg.k} {cfg.dtype}",
+                   "T": cfg.T, "d": cfg.d, "I": cfg.I, "N": cfg.N, "Z": cfg.Z, "k": cfg.k,
+                   "ffn_pairs": alg["P"], "touched_experts": alg["touched"]},
+        "roofline": roofline,
+        "step_hbm_frac": round(alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "step_mfma_frac": round(alg["step_flops"] / step_s / 1e12 / peak_tf, 4),
+        "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        ntok = args.cpu_tokens or {"prod": 128, "skewed": 128, "decode": 128, "small": 512,
+                                   "tiny": 64}[cfg.name]
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, min(ntok, cfg.T))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

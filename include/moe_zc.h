@@ -1,0 +1,148 @@
+/*
+ * moe_zc.h -- C ABI of the MI355X (gfx950) zero-computation-expert MoE forward.
+ *
+ * The operation (LongCat-Flash technical-report summary page, section 2
+ * "architecture", item 1 "zero-computation experts"; model configuration in
+ * the same section): every token is routed among N FFN experts and Z
+ * zero-computation experts.  A zero-computation expert returns its input
+ * unchanged and costs no compute.  An expert-specific bias, driven by a
+ * controller from the per-expert selection counts, shifts the routing scores
+ * so the share of FFN vs zero experts stays on target.
+ *
+ * Concretely, for each token t with activations x[t] (length d):
+ *   1. l[e]   = <x[t], W_router[e]>          for all E = N + Z experts
+ *      p     = softmax(l)                    (over all E, fp32)
+ *   2. s[e]   = p[e] + bias[e]               (selection only)
+ *      idx   = the k experts of largest s, by s descending, ties -> lower e
+ *      gate_j = p[idx_j]                     (unbiased, no renormalisation)
+ *   3. FFN expert e < N: y_e = W_down[e] (silu(W_gate[e] x) * (W_up[e] x)),
+ *      silu(z) = z / (1 + exp(-z))           (SwiGLU, three matrices, no bias)
+ *   4. zero expert e >= N: contributes gate * x (identity)
+ *   5. out[t] = (sum of zero-slot gates) * x[t] + sum_j gate_j * y_{idx_j},
+ *      counts[e] = number of (t, j) with idx_j == e   (sums to T * k)
+ * Expert numbering: 0 .. N-1 are FFN experts, N .. N+Z-1 zero experts.
+ *
+ * Precision: storage in the dims' dtype (fp32 or bfloat16); products are
+ * accumulated in fp32; for bfloat16 the SwiGLU activations and the expert
+ * outputs are rounded to bfloat16 between the two expert GEMMs and before
+ * the combine; the combine sums in fp32 in ascending slot order and rounds
+ * once.  The combine uses no atomics: results are run-to-run bit-identical.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronises, keeps no mutable global
+ *     state, and is re-entrant per stream.  `stream` is a hipStream_t
+ *     (NULL = the default stream).
+ *   - Work is enqueued asynchronously on `stream`.  Arguments are validated
+ *     before anything is enqueued; on a validation error nothing is written.
+ *     A failed launch returns MOE_ZC_EHIP.  Faults inside kernels surface at
+ *     the caller's next synchronisation.
+ */
+#ifndef MOE_ZC_H
+#define MOE_ZC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_ZC_F32 = 0, MOE_ZC_BF16 = 1 } moe_zc_dtype;
+
+typedef enum {
+  MOE_ZC_OK = 0,
+  MOE_ZC_EINVAL = -1, /* a size, count or pointer argument is invalid        */
+  MOE_ZC_EDTYPE = -2, /* dtype is neither MOE_ZC_F32 nor MOE_ZC_BF16          */
+  MOE_ZC_EALIGN = -3, /* a pointer is misaligned, or d / I not a multiple of 8 */
+  MOE_ZC_ENOSPC = -4, /* workspace missing or smaller than the query          */
+  MOE_ZC_EHIP = -5    /* a HIP launch failed                                  */
+} moe_zc_status;
+
+/* Problem sizes.  Limits: T >= 0; d >= 8 and I >= 8, both multiples of 8;
+ * N >= 0, Z >= 0, 1 <= N + Z <= 2048; 1 <= k <= min(64, N + Z);
+ * T * k < 2^31; T * d and I * d (times the element size) below 2 GiB.
+ * I is ignored when N == 0. */
+typedef struct {
+  int64_t T;     /* tokens                                   */
+  int32_t d;     /* model width                               */
+  int32_t I;     /* FFN expert width                          */
+  int32_t N;     /* FFN experts                               */
+  int32_t Z;     /* zero-computation experts                  */
+  int32_t k;     /* experts per token                         */
+  int32_t dtype; /* moe_zc_dtype of x, weights and out        */
+} moe_zc_dims;
+
+/* Bytes of device workspace moe_zc_forward needs for `dims` (worst case:
+ * every slot an FFN expert).  Returns 0 for invalid dims. */
+size_t moe_zc_workspace_bytes(const moe_zc_dims *dims);
+
+/* The forward pass, steps 1-5 above.
+ *   x          [T, d]        dtype, row-major, 16-byte aligned
+ *   W_router   [N+Z, d]      dtype, row e = expert e
+ *   bias       [N+Z]         fp32, used for selection only
+ *   W_gate     [N, I, d]     dtype (NULL allowed when N == 0)
+ *   W_up       [N, I, d]     dtype (NULL allowed when N == 0)
+ *   W_down     [N, d, I]     dtype (NULL allowed when N == 0)
+ *   out        [T, d]        dtype, overwritten; must not overlap x
+ *   counts     [N+Z]         int32, overwritten (zeroed when T == 0)
+ *   topk_idx   [T, k]        int32, nullable; biased score descending,
+ *                            ties -> lower index
+ *   topk_gate  [T, k]        fp32, nullable; unbiased probabilities
+ *   workspace  >= moe_zc_workspace_bytes(dims) bytes, 256-byte aligned;
+ *              its contents on entry are ignored
+ * Returns a moe_zc_status. */
+int moe_zc_forward(const moe_zc_dims *dims, const void *x, const void *W_router,
+                   const float *bias, const void *W_gate, const void *W_up, const void *W_down,
+                   void *out, int32_t *counts, int32_t *topk_idx, float *topk_gate,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static English text for a status code (never NULL). */
+const char *moe_zc_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Per-stage timing (measurement aid).  A timer owns HIP events for up to
+ * `max_calls` forward calls; moe_zc_forward_timed records an event before
+ * the first and after every stage on `stream`.  moe_zc_timer_read waits for
+ * the recorded events and returns, per stage, the summed milliseconds over
+ * all recorded calls.  A timer is used by one stream at a time.
+ * ------------------------------------------------------------------------ */
+enum {
+  MOE_ZC_STAGE_ROUTER = 0,  /* step 1: router logits GEMM             */
+  MOE_ZC_STAGE_TOPK = 1,    /* steps 1-2: softmax, bias, top-k        */
+  MOE_ZC_STAGE_SCAN = 2,    /* step 5 counts + dispatch offsets       */
+  MOE_ZC_STAGE_PERMUTE = 3, /* dispatch: token -> expert row map      */
+  MOE_ZC_STAGE_GATE_UP = 4, /* step 3: gate/up GEMM + SwiGLU          */
+  MOE_ZC_STAGE_DOWN = 5,    /* step 3: down GEMM                      */
+  MOE_ZC_STAGE_COMBINE = 6, /* steps 4-5: zero experts + combine      */
+  MOE_ZC_NSTAGES = 7
+};
+
+typedef struct moe_zc_timer moe_zc_timer;
+
+/* Creates a timer (HIP events on the current device).  MOE_ZC_EINVAL if
+ * max_calls < 1 or out is NULL, MOE_ZC_EHIP if event creation fails. */
+int moe_zc_timer_create(int max_calls, moe_zc_timer **out);
+
+/* As moe_zc_forward; also records events into `timer` (MOE_ZC_ENOSPC once
+ * it holds max_calls calls; nothing is enqueued then). */
+int moe_zc_forward_timed(const moe_zc_dims *dims, const void *x, const void *W_router,
+                         const float *bias, const void *W_gate, const void *W_up,
+                         const void *W_down, void *out, int32_t *counts, int32_t *topk_idx,
+                         float *topk_gate, void *workspace, size_t workspace_bytes, void *stream,
+                         moe_zc_timer *timer);
+
+/* Waits for the recorded events; writes the number of recorded calls and
+ * the per-stage millisecond sums (ms[MOE_ZC_NSTAGES]). */
+int moe_zc_timer_read(moe_zc_timer *timer, int *ncalls, float *ms);
+
+/* Forgets the recorded calls. */
+void moe_zc_timer_reset(moe_zc_timer *timer);
+
+void moe_zc_timer_destroy(moe_zc_timer *timer);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ZC_H */

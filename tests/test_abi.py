@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects every invalid argument before enqueueing work.
+
+Every call here fails validation, so no kernel is ever launched (the fake
+pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import zero_computation_expert_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_zc.h")
+
+A = 1 << 20  # a 16- and 256-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_zc_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = moe.lib()
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        s = moe.status_string(code)
+        assert s and s != "unknown status"
+    assert moe.status_string(42) == "unknown status"
+
+
+def call(dims, x=A, wr=2 * A, bias=3 * A, wg=4 * A, wu=5 * A, wd=6 * A, out=7 * A, counts=8 * A,
+         idx=None, gate=None, ws=16 * A, ws_bytes=None):
+    lib = moe.lib()
+    if ws_bytes is None:
+        ws_bytes = lib.moe_zc_workspace_bytes(ctypes.byref(dims)) if dims else 0
+    dp = ctypes.byref(dims) if dims is not None else None
+    st = lib.moe_zc_forward(dp, x, wr, bias, wg, wu, wd, out, counts, idx, gate, ws, ws_bytes, None)
+    assert st != 0, "a test call passed validation: it would have launched work"
+    return st
+
+
+def D(T=64, d=128, I=64, N=8, Z=4, k=2, dtype=moe.BF16):
+    return moe.make_dims(T, d, I, N, Z, k, dtype)
+
+
+EINVAL, EDTYPE, EALIGN, ENOSPC = -1, -2, -3, -4
+
+
+@pytest.mark.parametrize("dims,expect", [
+    (D(dtype=7), EDTYPE),
+    (D(T=-1), EINVAL),
+    (D(k=0), EINVAL),
+    (D(k=13), EINVAL),                       # k > N + Z
+    (D(N=0, Z=0), EINVAL),                   # no experts
+    (D(N=-1), EINVAL),
+    (D(N=2000, Z=49, k=2), EINVAL),          # N + Z > 2048
+    (D(N=100, Z=0, k=65), EINVAL),           # k > 64
+    (D(d=0), EINVAL),
+    (D(I=0), EINVAL),
+    (D(d=100), EALIGN),                      # not a multiple of 8
+    (D(I=60), EALIGN),
+    (D(T=1 << 28, k=8), EINVAL),             # T * k >= 2^31
+    (D(T=1 << 20, d=1024, k=2), EINVAL),     # x is 2 GiB of bf16
+    (D(I=1 << 17, d=8192), EINVAL),          # one expert matrix is 2 GiB
+])
+def test_invalid_dims(dims, expect):
+    assert moe.lib().moe_zc_workspace_bytes(ctypes.byref(dims)) == 0
+    assert call(dims, ws_bytes=1 << 40) == expect
+
+
+def test_null_dims():
+    assert moe.lib().moe_zc_workspace_bytes(None) == 0
+    assert call(None, ws_bytes=1 << 40) == EINVAL
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({"counts": None}, EINVAL),
+    ({"x": None}, EINVAL),
+    ({"wr": None}, EINVAL),
+    ({"bias": None}, EINVAL),
+    ({"out": None}, EINVAL),
+    ({"wg": None}, EINVAL),
+    ({"wd": None}, EINVAL),
+    ({"out": A + 64}, EINVAL),               # out overlaps x
+    ({"x": A + 8}, EALIGN),
+    ({"wu": 5 * A + 4}, EALIGN),
+    ({"bias": 3 * A + 2}, EALIGN),
+    ({"idx": 9 * A + 1}, EALIGN),
+    ({"ws": None}, ENOSPC),
+    ({"ws": 16 * A + 16}, EALIGN),           # workspace must be 256-byte aligned
+])
+def test_invalid_pointers(kw, expect):
+    assert call(D(), **kw) == expect
+
+
+def test_workspace_too_small():
+    dims = D()
+    need = moe.lib().moe_zc_workspace_bytes(ctypes.byref(dims))
+    assert need > 0
+    assert call(dims, ws_bytes=need - 1) == ENOSPC
+
+
+def test_workspace_grows_with_tokens_and_covers_the_worst_case():
+    lib = moe.lib()
+    small = lib.moe_zc_workspace_bytes(ctypes.byref(D(T=64)))
+    big = lib.moe_zc_workspace_bytes(ctypes.byref(D(T=4096)))
+    assert big > small > 0
+    # H and Y for every slot routed to an FFN expert, in bf16
+    T, d, I, k = 4096, 128, 64, 2
+    assert big >= T * k * (I + d) * 2
+
+
+def test_weights_may_be_null_without_ffn_experts():
+    # N = 0: null weights pass; the call still fails on the missing workspace
+    assert call(D(N=0, Z=4, k=2), wg=None, wu=None, wd=None, ws=None, ws_bytes=0) == ENOSPC
+
+
+def test_product_package_has_no_cpu_path():
+    """The binding marshals arguments only: it imports neither the oracle nor
+    numpy, and it has no compute of its own."""
+    src = open(os.path.join(ROOT, "zero_computation_expert_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("no fallback", "")
+    assert "import numpy" not in src
+    for f in os.listdir(os.path.join(ROOT, "zero_computation_expert_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "zero_computation_expert_amd", "csrc", f)).read()

@@ -1,0 +1,184 @@
+"""GPU parity against the CPU oracle on shapes the oracle finishes in seconds
+(full element-by-element comparison), plus the method's edge cases.  All
+calls go through the C ABI (zero_computation_expert_amd.forward)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+moe = pytest.importorskip("zero_computation_expert_amd")
+
+
+def run_gpu(cfg, inp, bias=None, poison=False, **over):
+    dev = "cuda:0"
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+    def dt(a):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if cfg.dtype == "bf16":
+            t = t.view(torch.bfloat16)
+        return t.to(dev)
+
+    x = dt(inp["x"])
+    b = torch.from_numpy(np.ascontiguousarray(inp["bias"] if bias is None else bias)).to(dev)
+    ws = None
+    if poison:
+        nbytes = moe.workspace_bytes(cfg.T, cfg.d, cfg.I, cfg.N, cfg.Z, cfg.k,
+                                     moe.F32 if cfg.dtype == "f32" else moe.BF16)
+        ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=dev)  # NaN bytes
+    out, cnt, idx, gate = moe.forward(x, dt(inp["W_router"]), b, dt(over.get("W_gate", inp["W_gate"])),
+                                      dt(over.get("W_up", inp["W_up"])),
+                                      dt(over.get("W_down", inp["W_down"])),
+                                      cfg.N, cfg.Z, cfg.k, workspace=ws)
+    torch.cuda.synchronize()
+    assert out.dtype == tdt
+    return P.to_np(out), P.to_np(cnt), P.to_np(idx), P.to_np(gate)
+
+
+def oracle_routing(cfg, inp, bias=None):
+    logits = oracle.router_logits(inp["x"], inp["W_router"], cfg.dtype)
+    b = inp["bias"] if bias is None else bias
+    return oracle.route_from_logits(logits, b, cfg.k)
+
+
+def full_check(cfg, inp, bias=None, poison=False):
+    print(f"[parity] {cfg}", flush=True)
+    b = inp["bias"] if bias is None else bias
+    out, cnt, idx, gate = run_gpu(cfg, inp, bias=b, poison=poison)
+    oidx, ogate, omargin, oprobs = oracle_routing(cfg, inp, b)
+    info = P.check_routing(cfg, b, idx, gate, cnt, oidx, oprobs, omargin)
+    P.check_counts_against_oracle(cfg, idx, cnt, oidx, omargin)
+    ref = P.reference_outputs(cfg, inp, idx, oprobs)
+    got = P.out_as_f32(out, cfg.dtype)
+    assert np.isfinite(got).all()
+    err = P.rel_frob(got, ref)
+    print(f"[parity] rel_frob={err:.3e} gate_err={info['gate_err']:.2e} "
+          f"near_ties={info['near_ties']}", flush=True)
+    assert err <= P.OUT_TOL[cfg.dtype]
+    return out, cnt, idx, gate
+
+
+# tiny config of the workload table (fp32) and ragged shapes that span several
+# tiles with partial row blocks, partial token chunks and a K tail
+RAGGED = [
+    synth.TINY,
+    synth.Config("ragged_bf16", T=300, d=256, I=192, N=10, Z=5, k=4, dtype="bf16", seed=3),
+    synth.Config("ragged_f32", T=300, d=256, I=192, N=10, Z=5, k=4, dtype="f32", seed=3),
+    synth.Config("ktail_bf16", T=77, d=200, I=72, N=5, Z=3, k=3, dtype="bf16", seed=4),
+    synth.Config("ktail_f32", T=77, d=200, I=72, N=5, Z=3, k=3, dtype="f32", seed=4),
+    synth.Config("wide_bf16", T=520, d=384, I=320, N=40, Z=20, k=8, dtype="bf16", seed=5,
+                 bias_lo=-0.02, bias_hi=0.02),
+    synth.Config("decodeish_bf16", T=9, d=512, I=256, N=48, Z=16, k=6, dtype="bf16", seed=6),
+]
+
+
+@pytest.mark.parametrize("cfg", RAGGED, ids=lambda c: c.name)
+def test_parity_full(cfg):
+    full_check(cfg, synth.host_inputs(cfg), poison=True)
+
+
+def test_deterministic_bitwise():
+    cfg = RAGGED[1]
+    inp = synth.host_inputs(cfg)
+    a = run_gpu(cfg, inp)
+    b = run_gpu(cfg, inp, poison=True)
+    for u, v in zip(a, b):
+        assert (u == v).all()
+
+
+def test_token_permutation_equivariance():
+    cfg = RAGGED[1]
+    inp = synth.host_inputs(cfg)
+    a = run_gpu(cfg, inp)
+    perm = np.random.default_rng(0).permutation(cfg.T)
+    inp2 = dict(inp, x=inp["x"][perm])
+    b = run_gpu(cfg, inp2)
+    assert (b[2] == a[2][perm]).all() and (b[1] == a[1]).all()
+    assert P.rel_frob(P.out_as_f32(b[0], cfg.dtype), P.out_as_f32(a[0], cfg.dtype)[perm]) < 1e-6
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_all_zero_routing_is_gate_sum_times_x(dt):
+    """Bias +10 on every zero expert (Z >= k): no FFN expert runs, out = (sum of
+    gates) * x.  The FFN weights are NaN: reading them would show."""
+    cfg = synth.Config("allzero", T=130, d=128, I=64, N=6, Z=5, k=4, dtype=dt, seed=8)
+    inp = synth.host_inputs(cfg)
+    b = np.zeros(cfg.E, np.float32)
+    b[cfg.N:] = 10.0
+    nan = np.full_like(inp["W_gate"], 0x7FC0 if dt == "bf16" else np.float32("nan"))
+    inp_nan = dict(inp, W_gate=nan, W_up=nan, W_down=nan.copy())
+    out, cnt, idx, gate = run_gpu(cfg, inp_nan, bias=b)
+    assert (idx >= cfg.N).all() and (cnt[:cfg.N] == 0).all()
+    x = P.out_as_f32(inp["x"], dt)
+    zs = gate.astype(np.float64).sum(1)
+    ref = zs[:, None] * x
+    assert P.rel_frob(P.out_as_f32(out, dt), ref) <= P.OUT_TOL[dt]
+    assert np.isfinite(P.out_as_f32(out, dt)).all()
+
+
+def test_no_ffn_experts():
+    cfg = synth.Config("n0", T=70, d=64, I=8, N=0, Z=6, k=3, dtype="bf16", seed=2)
+    x, wr, bias = synth.host_x(cfg), synth.host_router(cfg), synth.host_bias(cfg)
+    inp = {"x": x, "W_router": wr, "bias": bias, "W_gate": None, "W_up": None, "W_down": None}
+    out, cnt, idx, gate = run_gpu(cfg, inp)
+    oidx, ogate, omargin, oprobs = oracle_routing(cfg, inp)
+    P.check_routing(cfg, bias, idx, gate, cnt, oidx, oprobs, omargin)
+    ref = gate.astype(np.float64).sum(1)[:, None] * synth.bf16_bits_to_f32(x)
+    assert P.rel_frob(P.out_as_f32(out, "bf16"), ref) <= 2e-2
+
+
+def test_z0_and_k_equals_E():
+    full_check(synth.Config("z0", T=100, d=128, I=64, N=7, Z=0, k=3, dtype="f32", seed=9),
+               synth.host_inputs(synth.Config("z0", T=100, d=128, I=64, N=7, Z=0, k=3,
+                                              dtype="f32", seed=9)))
+    cfg = synth.Config("kE", T=50, d=64, I=32, N=5, Z=3, k=8, dtype="bf16", seed=10)
+    _, cnt, _, _ = full_check(cfg, synth.host_inputs(cfg))
+    assert (cnt == cfg.T).all()
+
+
+def test_single_hot_expert_spans_many_chunks():
+    """Bias +10 on FFN expert 3: every token picks it (M_e = T, several
+    128-row chunks), the rest of the slots route normally."""
+    cfg = synth.Config("hot", T=700, d=256, I=128, N=12, Z=4, k=3, dtype="bf16", seed=11)
+    inp = synth.host_inputs(cfg)
+    b = inp["bias"].copy()
+    b[3] = 10.0
+    _, cnt, idx, _ = full_check(cfg, inp, bias=b)
+    assert cnt[3] == cfg.T and (idx[:, 0] == 3).all()
+
+
+def test_empty_and_single_token():
+    cfg = synth.Config("one", T=1, d=64, I=16, N=4, Z=2, k=2, dtype="bf16", seed=12)
+    full_check(cfg, synth.host_inputs(cfg))
+    cfg0 = cfg.with_(T=0)
+    dev = "cuda:0"
+    x = torch.empty((0, cfg.d), dtype=torch.bfloat16, device=dev)
+    w = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device=dev)
+    cnt = torch.full((cfg.E,), 7, dtype=torch.int32, device=dev)
+    out, c, _, _ = moe.forward(x, w(cfg.E, cfg.d), torch.zeros(cfg.E, device=dev),
+                               w(cfg.N, cfg.I, cfg.d), w(cfg.N, cfg.I, cfg.d),
+                               w(cfg.N, cfg.d, cfg.I), cfg0.N, cfg0.Z, cfg0.k, counts=cnt)
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.d) and (c.cpu() == 0).all()
+
+
+def test_stage_timer_records_every_stage():
+    cfg = RAGGED[1]
+    inp = synth.host_inputs(cfg)
+    dev = "cuda:0"
+    t = lambda a: torch.from_numpy(a).view(torch.bfloat16).to(dev)
+    timer = moe.Timer(4)
+    for _ in range(3):
+        moe.forward(t(inp["x"]), t(inp["W_router"]), torch.from_numpy(inp["bias"]).to(dev),
+                    t(inp["W_gate"]), t(inp["W_up"]), t(inp["W_down"]), cfg.N, cfg.Z, cfg.k,
+                    timer=timer)
+    n, ms = timer.read()
+    assert n == 3 and all(v >= 0 for v in ms.values()) and ms["gate_up"] > 0
+    timer.close()

@@ -1,0 +1,177 @@
+"""Python binding of the MI355X zero-computation-expert MoE forward.
+
+Argument marshalling only: every step of the forward runs in the HIP kernels
+of ``_moe_zc.so`` behind the C ABI declared in ``include/moe_zc.h``.  Torch
+tensors serve as device memory and torch's current stream as the HIP
+stream.  There is no fallback: if the library is missing or no GPU is
+visible, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_moe_zc.so")
+
+F32, BF16 = 0, 1
+STATUS = {0: "MOE_ZC_OK", -1: "MOE_ZC_EINVAL", -2: "MOE_ZC_EDTYPE", -3: "MOE_ZC_EALIGN",
+          -4: "MOE_ZC_ENOSPC", -5: "MOE_ZC_EHIP"}
+STAGES = ("router", "topk", "scan", "permute", "gate_up", "down", "combine")
+EXPORTS = ("moe_zc_workspace_bytes", "moe_zc_forward", "moe_zc_status_string",
+           "moe_zc_timer_create", "moe_zc_forward_timed", "moe_zc_timer_read",
+           "moe_zc_timer_reset", "moe_zc_timer_destroy")
+
+
+class MoeZcError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("Z", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load ``_moe_zc.so`` (built by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        dims_p = ctypes.POINTER(Dims)
+        L.moe_zc_workspace_bytes.restype = sz
+        L.moe_zc_workspace_bytes.argtypes = [dims_p]
+        fwd = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_zc_forward.restype = ctypes.c_int
+        L.moe_zc_forward.argtypes = fwd
+        L.moe_zc_forward_timed.restype = ctypes.c_int
+        L.moe_zc_forward_timed.argtypes = fwd + [vp]
+        L.moe_zc_status_string.restype = ctypes.c_char_p
+        L.moe_zc_status_string.argtypes = [ctypes.c_int]
+        L.moe_zc_timer_create.restype = ctypes.c_int
+        L.moe_zc_timer_create.argtypes = [ctypes.c_int, ctypes.POINTER(vp)]
+        L.moe_zc_timer_read.restype = ctypes.c_int
+        L.moe_zc_timer_read.argtypes = [vp, ctypes.POINTER(ctypes.c_int),
+                                        ctypes.POINTER(ctypes.c_float)]
+        L.moe_zc_timer_reset.restype = None
+        L.moe_zc_timer_reset.argtypes = [vp]
+        L.moe_zc_timer_destroy.restype = None
+        L.moe_zc_timer_destroy.argtypes = [vp]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_zc_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoeZcError(status, status_string(status))
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    return 99  # rejected by the library (MOE_ZC_EDTYPE)
+
+
+def make_dims(T, d, I, N, Z, k, dtype: int) -> Dims:
+    return Dims(int(T), int(d), int(I), int(N), int(Z), int(k), int(dtype))
+
+
+def workspace_bytes(T, d, I, N, Z, k, dtype: int) -> int:
+    return int(lib().moe_zc_workspace_bytes(ctypes.byref(make_dims(T, d, I, N, Z, k, dtype))))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    p = t.data_ptr()
+    return p if p != 0 else None
+
+
+class Timer:
+    """Per-stage HIP-event timer over up to ``max_calls`` forward calls."""
+
+    def __init__(self, max_calls: int):
+        h = ctypes.c_void_p()
+        _check(lib().moe_zc_timer_create(int(max_calls), ctypes.byref(h)))
+        self.handle = h
+
+    def read(self):
+        """Synchronises on the events; returns (ncalls, {stage: total ms})."""
+        n = ctypes.c_int()
+        ms = (ctypes.c_float * len(STAGES))()
+        _check(lib().moe_zc_timer_read(self.handle, ctypes.byref(n), ms))
+        return n.value, dict(zip(STAGES, [float(v) for v in ms]))
+
+    def reset(self):
+        lib().moe_zc_timer_reset(self.handle)
+
+    def close(self):
+        if self.handle:
+            lib().moe_zc_timer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def forward(x, W_router, bias, W_gate, W_up, W_down, N: int, Z: int, k: int, *,
+            out=None, counts=None, topk_idx=None, topk_gate=None, workspace=None,
+            stream=None, timer: Optional[Timer] = None, want_routing: bool = True):
+    """Runs moe_zc_forward on torch device tensors.
+
+    x [T, d] and the weights share one dtype (float32 or bfloat16); W_gate and
+    W_up are [N, I, d], W_down [N, d, I]; bias is float32 [N+Z].  Returns
+    (out, counts, topk_idx, topk_gate); the last two are None unless
+    ``want_routing``.  Output buffers and the workspace are allocated with
+    torch when not given.
+    """
+    import torch
+
+    T, d = x.shape
+    I = W_gate.shape[1] if (W_gate is not None and N > 0) else 0
+    dt = _dtype_code(x)
+    dims = make_dims(T, d, I, N, Z, k, dt)
+    dev = x.device
+    if out is None:
+        out = torch.empty_like(x)
+    if counts is None:
+        counts = torch.empty(N + Z, dtype=torch.int32, device=dev)
+    if want_routing:
+        if topk_idx is None:
+            topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        if topk_gate is None:
+            topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        nbytes = int(lib().moe_zc_workspace_bytes(ctypes.byref(dims)))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    args = [ctypes.byref(dims), _ptr(x), _ptr(W_router), _ptr(bias), _ptr(W_gate), _ptr(W_up),
+            _ptr(W_down), _ptr(out), _ptr(counts), _ptr(topk_idx), _ptr(topk_gate),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), stream]
+    if timer is None:
+        st = lib().moe_zc_forward(*args)
+    else:
+        st = lib().moe_zc_forward_timed(*args, timer.handle)
+    _check(st)
+    return out, counts, topk_idx, topk_gate

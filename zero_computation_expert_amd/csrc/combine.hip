@@ -1,0 +1,101 @@
+// combine.hip -- steps 4-5 of the zero-computation-expert MoE forward:
+//   out[t] = (sum of gates of zero-expert slots) * x[t] + sum_j gate_j * Y[rowmap[t, j]]
+// A zero-computation expert returns its input and costs nothing (LongCat-Flash
+// summary page, section 2 "architecture", item 1), so its whole contribution
+// folds into one scale of x.  FFN terms are added in ascending slot order in
+// fp32 and rounded once; no atomics, so the output is run-to-run identical
+// (the same page, section 1, asks for deterministic computation).
+#include "moe_zc_internal.h"
+
+namespace moezc {
+
+template <typename T>
+struct Vec16;  // 16 bytes of T
+template <>
+struct Vec16<bf16_t> {
+  static constexpr int n = 8;
+  static __device__ __forceinline__ void unpack(const uint4 &v, float *f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ uint4 pack(const float *f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(f[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(f[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <>
+struct Vec16<float> {
+  static constexpr int n = 4;
+  static __device__ __forceinline__ void unpack(const uint4 &v, float *f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  static __device__ __forceinline__ uint4 pack(const float *f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+};
+
+// One block per token; each thread handles 16-byte column pieces.
+template <typename T>
+__global__ void __launch_bounds__(256) combine_kernel(const T *__restrict__ x,
+                                                      const T *__restrict__ y,
+                                                      const int32_t *__restrict__ rowmap,
+                                                      const float *__restrict__ gate, int d,
+                                                      int k, T *__restrict__ out) {
+  constexpr int VN = Vec16<T>::n;
+  __shared__ int s_row[kMaxK];
+  __shared__ float s_gate[kMaxK];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < k) {
+    s_row[threadIdx.x] = rowmap[t * k + threadIdx.x];
+    s_gate[threadIdx.x] = gate[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  float zsum = 0.0f;
+  for (int j = 0; j < k; ++j)
+    if (s_row[j] < 0) zsum += s_gate[j];
+  const int npieces = d / VN;
+  for (int c = threadIdx.x; c < npieces; c += blockDim.x) {
+    float acc[VN], v[VN];
+    Vec16<T>::unpack(*reinterpret_cast<const uint4 *>(x + t * d + c * VN), v);
+#pragma unroll
+    for (int i = 0; i < VN; ++i) acc[i] = zsum * v[i];
+    for (int j = 0; j < k; ++j) {
+      const int row = s_row[j];
+      if (row < 0) continue;
+      const float gj = s_gate[j];
+      Vec16<T>::unpack(*reinterpret_cast<const uint4 *>(y + static_cast<int64_t>(row) * d + c * VN),
+                       v);
+#pragma unroll
+      for (int i = 0; i < VN; ++i) acc[i] += gj * v[i];
+    }
+    *reinterpret_cast<uint4 *>(out + t * d + c * VN) = Vec16<T>::pack(acc);
+  }
+}
+
+hipError_t launch_combine(const Plan &p, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(p.T)), block(256);
+  if (p.dtype == MOE_ZC_BF16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, s,
+                       static_cast<const bf16_t *>(p.x), static_cast<const bf16_t *>(p.y),
+                       p.rowmap, p.gate, p.d, p.k, static_cast<bf16_t *>(p.out));
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, static_cast<const float *>(p.x),
+                       static_cast<const float *>(p.y), p.rowmap, p.gate, p.d, p.k,
+                       static_cast<float *>(p.out));
+  return hipGetLastError();
+}
+
+}  // namespace moezc

@@ -1,0 +1,286 @@
+// moe_zc.hip -- host side of the C ABI declared in include/moe_zc.h:
+// argument validation, workspace layout and the ordered launch of the
+// forward's kernels on the caller's stream (no allocation, no sync).
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "moe_zc_internal.h"
+
+namespace moezc {
+
+static inline size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+static bool dims_ok(const moe_zc_dims *dm, int *status) {
+  if (dm == nullptr) {
+    *status = MOE_ZC_EINVAL;
+    return false;
+  }
+  if (dm->dtype != MOE_ZC_F32 && dm->dtype != MOE_ZC_BF16) {
+    *status = MOE_ZC_EDTYPE;
+    return false;
+  }
+  const int64_t E = static_cast<int64_t>(dm->N) + dm->Z;
+  if (dm->T < 0 || dm->N < 0 || dm->Z < 0 || E < 1 || E > kMaxE || dm->k < 1 || dm->k > E ||
+      dm->k > kMaxK || dm->d < 8 || (dm->N > 0 && dm->I < 8) ||
+      dm->T * static_cast<int64_t>(dm->k) >= (int64_t(1) << 31)) {
+    *status = MOE_ZC_EINVAL;
+    return false;
+  }
+  // The expert GEMMs address x and one expert matrix through 32-bit buffer
+  // offsets: both must stay below 2 GiB.
+  const int64_t es = dm->dtype == MOE_ZC_BF16 ? 2 : 4;
+  if (dm->T * dm->d * es >= (int64_t(1) << 31) ||
+      (dm->N > 0 && static_cast<int64_t>(dm->I) * dm->d * es >= (int64_t(1) << 31))) {
+    *status = MOE_ZC_EINVAL;
+    return false;
+  }
+  if (dm->d % 8 != 0 || (dm->N > 0 && dm->I % 8 != 0)) {
+    *status = MOE_ZC_EALIGN;
+    return false;
+  }
+  *status = MOE_ZC_OK;
+  return true;
+}
+
+// Workspace layout; returns the total size.  With base == nullptr only sizes.
+static size_t layout(const moe_zc_dims *dm, char *base, Plan *p) {
+  const int64_t T = dm->T;
+  const int E = dm->N + dm->Z;
+  const int64_t nblk = (T + kTokPerBlk - 1) / kTokPerBlk;
+  const int64_t pmax = T * std::min(dm->k, dm->N);
+  const size_t es = dm->dtype == MOE_ZC_BF16 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *ptr = base ? base + off : nullptr;
+    off = align_up(off + bytes);
+    return ptr;
+  };
+  char *logits = take(static_cast<size_t>(T) * E * 4);
+  char *blockhist = take(static_cast<size_t>(nblk) * E * 4);
+  char *offs = take(static_cast<size_t>(dm->N + 1) * 4);
+  char *chunk_off = take(static_cast<size_t>(dm->N + 1) * 4);
+  char *meta = take(64);
+  char *idx = take(static_cast<size_t>(T) * dm->k * 4);
+  char *gate = take(static_cast<size_t>(T) * dm->k * 4);
+  char *rowmap = take(static_cast<size_t>(T) * dm->k * 4);
+  char *tok = take(static_cast<size_t>(pmax) * 4);
+  char *h = take(static_cast<size_t>(pmax) * (dm->N > 0 ? dm->I : 0) * es);
+  char *y = take(static_cast<size_t>(pmax) * dm->d * es);
+  if (p) {
+    p->logits = reinterpret_cast<float *>(logits);
+    p->blockhist = reinterpret_cast<int32_t *>(blockhist);
+    p->offs = reinterpret_cast<int32_t *>(offs);
+    p->chunk_off = reinterpret_cast<int32_t *>(chunk_off);
+    p->meta = reinterpret_cast<int32_t *>(meta);
+    p->idx = reinterpret_cast<int32_t *>(idx);
+    p->gate = reinterpret_cast<float *>(gate);
+    p->rowmap = reinterpret_cast<int32_t *>(rowmap);
+    p->tok = reinterpret_cast<int32_t *>(tok);
+    p->h = h;
+    p->y = y;
+  }
+  return off;
+}
+
+static bool aligned(const void *ptr, size_t a) {
+  return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0;
+}
+
+static bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace moezc
+
+struct moe_zc_timer {
+  int max_calls;
+  int ncalls;
+  hipEvent_t *ev;  // [max_calls][MOE_ZC_NSTAGES + 1]
+};
+
+using namespace moezc;
+
+static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_router,
+                        const float *bias, const void *w_gate, const void *w_up,
+                        const void *w_down, void *out, int32_t *counts, int32_t *topk_idx,
+                        float *topk_gate, void *workspace, size_t workspace_bytes, void *stream,
+                        moe_zc_timer *timer) {
+  int st;
+  if (!dims_ok(dm, &st)) return st;
+  const int64_t T = dm->T;
+  const size_t es = dm->dtype == MOE_ZC_BF16 ? 2 : 4;
+  const size_t xbytes = static_cast<size_t>(T) * dm->d * es;
+  if (counts == nullptr) return MOE_ZC_EINVAL;
+  if (T > 0) {
+    if (!x || !w_router || !bias || !out) return MOE_ZC_EINVAL;
+    if (dm->N > 0 && (!w_gate || !w_up || !w_down)) return MOE_ZC_EINVAL;
+    if (overlap(x, xbytes, out, xbytes)) return MOE_ZC_EINVAL;
+  }
+  const void *p16[] = {x, w_router, w_gate, w_up, w_down, out};
+  for (const void *ptr : p16)
+    if (ptr && !aligned(ptr, 16)) return MOE_ZC_EALIGN;
+  const void *p4[] = {bias, counts, topk_idx, topk_gate};
+  for (const void *ptr : p4)
+    if (ptr && !aligned(ptr, 4)) return MOE_ZC_EALIGN;
+  const size_t need = layout(dm, nullptr, nullptr);
+  if (T > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MOE_ZC_ENOSPC;
+    if (!aligned(workspace, 256)) return MOE_ZC_EALIGN;
+  }
+  if (timer && timer->ncalls >= timer->max_calls) return MOE_ZC_ENOSPC;
+
+  Plan p = {};
+  p.T = T;
+  p.d = dm->d;
+  p.I = dm->N > 0 ? dm->I : 0;
+  p.N = dm->N;
+  p.Z = dm->Z;
+  p.E = dm->N + dm->Z;
+  p.k = dm->k;
+  p.dtype = dm->dtype;
+  p.nblk = static_cast<int>((T + kTokPerBlk - 1) / kTokPerBlk);
+  p.pmax = T * std::min(dm->k, dm->N);
+  // Chunk height of the expert GEMMs: 128 token rows when experts receive
+  // many rows on average, else 32 (decode-shaped: weight streaming with few
+  // rows per expert wants occupancy, not tall tiles).
+  const int64_t avg_rows = dm->N > 0 ? p.pmax / dm->N : 0;
+  p.nbmax = avg_rows >= 48 ? 4 : 1;
+  p.x = x;
+  p.w_router = w_router;
+  p.w_gate = w_gate;
+  p.w_up = w_up;
+  p.w_down = w_down;
+  p.bias = bias;
+  p.out = out;
+  p.counts = counts;
+  layout(dm, static_cast<char *>(workspace), &p);
+  if (topk_idx) p.idx = topk_idx;
+  if (topk_gate) p.gate = topk_gate;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t *ev = timer ? timer->ev + static_cast<size_t>(timer->ncalls) * (MOE_ZC_NSTAGES + 1)
+                         : nullptr;
+  auto mark = [&](int i) -> bool {
+    return ev == nullptr || hipEventRecord(ev[i], s) == hipSuccess;
+  };
+
+  if (T == 0) {
+    if (launch_zero_counts(p, s) != hipSuccess) return MOE_ZC_EHIP;
+    if (timer) {
+      for (int i = 0; i <= MOE_ZC_NSTAGES; ++i)
+        if (!mark(i)) return MOE_ZC_EHIP;
+      timer->ncalls++;
+    }
+    return MOE_ZC_OK;
+  }
+
+  typedef hipError_t (*Launch)(const Plan &, hipStream_t);
+  const Launch stages[MOE_ZC_NSTAGES] = {launch_router_gemm, launch_topk, launch_scan,
+                                         launch_permute,     launch_gate_up, launch_down,
+                                         launch_combine};
+  if (!mark(0)) return MOE_ZC_EHIP;
+  for (int i = 0; i < MOE_ZC_NSTAGES; ++i) {
+    const bool ffn = i == MOE_ZC_STAGE_GATE_UP || i == MOE_ZC_STAGE_DOWN;
+    if (!(ffn && p.N == 0))
+      if (stages[i](p, s) != hipSuccess) return MOE_ZC_EHIP;
+    if (!mark(i + 1)) return MOE_ZC_EHIP;
+  }
+  if (timer) timer->ncalls++;
+  return MOE_ZC_OK;
+}
+
+extern "C" {
+
+size_t moe_zc_workspace_bytes(const moe_zc_dims *dims) {
+  int st;
+  if (!dims_ok(dims, &st)) return 0;
+  return layout(dims, nullptr, nullptr);
+}
+
+int moe_zc_forward(const moe_zc_dims *dims, const void *x, const void *W_router,
+                   const float *bias, const void *W_gate, const void *W_up, const void *W_down,
+                   void *out, int32_t *counts, int32_t *topk_idx, float *topk_gate,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  return forward_impl(dims, x, W_router, bias, W_gate, W_up, W_down, out, counts, topk_idx,
+                      topk_gate, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_zc_forward_timed(const moe_zc_dims *dims, const void *x, const void *W_router,
+                         const float *bias, const void *W_gate, const void *W_up,
+                         const void *W_down, void *out, int32_t *counts, int32_t *topk_idx,
+                         float *topk_gate, void *workspace, size_t workspace_bytes, void *stream,
+                         moe_zc_timer *timer) {
+  if (timer == nullptr) return MOE_ZC_EINVAL;
+  return forward_impl(dims, x, W_router, bias, W_gate, W_up, W_down, out, counts, topk_idx,
+                      topk_gate, workspace, workspace_bytes, stream, timer);
+}
+
+const char *moe_zc_status_string(int status) {
+  switch (status) {
+    case MOE_ZC_OK: return "ok";
+    case MOE_ZC_EINVAL: return "invalid argument (size, count or pointer)";
+    case MOE_ZC_EDTYPE: return "unsupported dtype";
+    case MOE_ZC_EALIGN: return "misaligned pointer, or d / I not a multiple of 8";
+    case MOE_ZC_ENOSPC: return "workspace missing or too small (or timer full)";
+    case MOE_ZC_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_zc_timer_create(int max_calls, moe_zc_timer **out) {
+  if (out == nullptr || max_calls < 1) return MOE_ZC_EINVAL;
+  *out = nullptr;
+  moe_zc_timer *t = new (std::nothrow) moe_zc_timer;
+  if (!t) return MOE_ZC_EINVAL;
+  const size_t n = static_cast<size_t>(max_calls) * (MOE_ZC_NSTAGES + 1);
+  t->ev = new (std::nothrow) hipEvent_t[n];
+  if (!t->ev) {
+    delete t;
+    return MOE_ZC_EINVAL;
+  }
+  t->max_calls = max_calls;
+  t->ncalls = 0;
+  for (size_t i = 0; i < n; ++i) {
+    if (hipEventCreate(&t->ev[i]) != hipSuccess) {
+      for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(t->ev[j]);
+      delete[] t->ev;
+      delete t;
+      return MOE_ZC_EHIP;
+    }
+  }
+  *out = t;
+  return MOE_ZC_OK;
+}
+
+int moe_zc_timer_read(moe_zc_timer *t, int *ncalls, float *ms) {
+  if (t == nullptr || ms == nullptr) return MOE_ZC_EINVAL;
+  for (int s = 0; s < MOE_ZC_NSTAGES; ++s) ms[s] = 0.0f;
+  for (int c = 0; c < t->ncalls; ++c) {
+    hipEvent_t *ev = t->ev + static_cast<size_t>(c) * (MOE_ZC_NSTAGES + 1);
+    if (hipEventSynchronize(ev[MOE_ZC_NSTAGES]) != hipSuccess) return MOE_ZC_EHIP;
+    for (int s = 0; s < MOE_ZC_NSTAGES; ++s) {
+      float v = 0.0f;
+      if (hipEventElapsedTime(&v, ev[s], ev[s + 1]) != hipSuccess) return MOE_ZC_EHIP;
+      ms[s] += v;
+    }
+  }
+  if (ncalls) *ncalls = t->ncalls;
+  return MOE_ZC_OK;
+}
+
+void moe_zc_timer_reset(moe_zc_timer *t) {
+  if (t) t->ncalls = 0;
+}
+
+void moe_zc_timer_destroy(moe_zc_timer *t) {
+  if (!t) return;
+  const size_t n = static_cast<size_t>(t->max_calls) * (MOE_ZC_NSTAGES + 1);
+  for (size_t i = 0; i < n; ++i) (void)hipEventDestroy(t->ev[i]);
+  delete[] t->ev;
+  delete t;
+}
+
+}  // extern "C"

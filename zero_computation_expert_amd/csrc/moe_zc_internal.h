@@ -1,0 +1,112 @@
+// moe_zc_internal.h -- device helpers and launcher declarations shared by the
+// HIP translation units of the MoE forward library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_zc.h"
+
+namespace moezc {
+
+constexpr int kWave = 64;
+constexpr int kTokPerBlk = 64;  // tokens per top-k / permutation block
+constexpr int kMaxE = 2048;     // experts the top-k kernel holds in registers
+constexpr int kMaxK = 64;       // slots per token (one lane per slot)
+
+// bfloat16 is carried as its 16-bit pattern.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bfloat16 (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static __device__ __forceinline__ float load(const float *p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+  static __device__ __forceinline__ float from_f32(float v) { return v; }
+};
+template <>
+struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t *p, int64_t i) {
+    return bf16_to_f32(p[i]);
+  }
+  static __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, kWave);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, kWave);
+    uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// ---- launchers (host side), one per stage ------------------------------
+struct Plan;  // defined in moe_zc.cpp
+
+hipError_t launch_router_gemm(const Plan &p, hipStream_t s);
+hipError_t launch_topk(const Plan &p, hipStream_t s);
+hipError_t launch_scan(const Plan &p, hipStream_t s);
+hipError_t launch_permute(const Plan &p, hipStream_t s);
+hipError_t launch_gate_up(const Plan &p, hipStream_t s);
+hipError_t launch_down(const Plan &p, hipStream_t s);
+hipError_t launch_combine(const Plan &p, hipStream_t s);
+hipError_t launch_zero_counts(const Plan &p, hipStream_t s);
+
+// Everything one forward call needs, resolved on the host.
+struct Plan {
+  // sizes
+  int64_t T;
+  int d, I, N, Z, E, k;
+  int dtype;  // moe_zc_dtype
+  int nblk;   // ceil(T / kTokPerBlk)
+  int64_t pmax;  // T * min(k, N): upper bound of (token, FFN expert) pairs
+  int nbmax;  // 32-token column blocks per GEMM chunk (1 or 4)
+  // caller tensors
+  const void *x, *w_router, *w_gate, *w_up, *w_down;
+  const float *bias;
+  void *out;
+  int32_t *counts;
+  int32_t *idx;   // caller's or workspace
+  float *gate;    // caller's or workspace
+  // workspace
+  float *logits;        // [T, E]
+  int32_t *blockhist;   // [nblk, E]: per-block counts, then exclusive prefixes
+  int32_t *offs;        // [N + 1] row offset of each FFN expert in permuted order
+  int32_t *chunk_off;   // [N + 1] exclusive prefix of GEMM chunks per expert
+  int32_t *meta;        // [0] total chunks, [1] total pairs P
+  int32_t *rowmap;      // [T, k] permuted row of slot (t, j), -1 for zero experts
+  int32_t *tok;         // [pmax] token of each permuted row
+  void *h;              // [pmax, I] SwiGLU activations
+  void *y;              // [pmax, d] expert outputs
+};
+
+}  // namespace moezc

@@ -1,0 +1,275 @@
+// route.hip -- steps 1-2 (softmax, selection bias, top-k, gates) and the
+// dispatch bookkeeping (selection counts, expert offsets, stable token ->
+// expert permutation) of the zero-computation-expert MoE forward.
+//
+// Method: LongCat-Flash technical-report summary page, section 2
+// "architecture", item 1 "zero-computation experts": tokens choose among N
+// FFN experts and Z zero experts; an expert-specific bias shifts the routing
+// scores to hold the FFN / zero selection ratio; the per-expert selection
+// counts are what the bias controller consumes.  Softmax over all experts,
+// the bias used for selection only, unbiased gates and the tie-break towards
+// the lower expert index are this library's readings of that passage.
+#include "moe_zc_internal.h"
+
+namespace moezc {
+
+// Order-preserving map of an fp32 score to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave per token.  Expert e lives in lane e % 64, register slot e / 64.
+// Selection key = (ordered score << 32) | (0xffffffff - e): the wave maximum
+// is the highest score and, among equal scores, the lowest index.  Key 0
+// marks a taken or absent expert (every real key is > 0).
+// The block (4 waves) covers kTokPerBlk consecutive tokens and writes its
+// per-expert selection histogram to blockhist[blockIdx.x].
+template <int VPL>
+__global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits,
+                                                   const float *__restrict__ bias, int64_t T,
+                                                   int E, int k, int32_t *__restrict__ idx_out,
+                                                   float *__restrict__ gate_out,
+                                                   int32_t *__restrict__ blockhist) {
+  __shared__ float s_bias[kMaxE];
+  __shared__ int s_hist[kMaxE];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    s_bias[e] = bias[e];
+    s_hist[e] = 0;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokPerBlk;
+
+  for (int tt = wave; tt < kTokPerBlk; tt += 4) {
+    const int64_t t = t0 + tt;
+    if (t >= T) break;
+    const float *lrow = logits + t * E;
+    float l[VPL];
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+      int e = s * kWave + lane;
+      l[s] = e < E ? lrow[e] : -INFINITY;
+    }
+    float m = l[0];
+#pragma unroll
+    for (int s = 1; s < VPL; ++s) m = fmaxf(m, l[s]);
+    m = wave_max(m);
+    float ex[VPL];
+    float part = 0.0f;
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+      int e = s * kWave + lane;
+      ex[s] = e < E ? expf(l[s] - m) : 0.0f;
+      part += ex[s];
+    }
+    const float sum = wave_sum(part);
+    float p[VPL];
+    uint64_t key[VPL];
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+      int e = s * kWave + lane;
+      p[s] = ex[s] / sum;
+      key[s] = e < E ? (static_cast<uint64_t>(ordered_bits(p[s] + s_bias[e])) << 32) |
+                           (0xffffffffu - static_cast<uint32_t>(e))
+                     : 0ull;
+    }
+    int my_idx = 0;
+    float my_gate = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int s = 1; s < VPL; ++s) best = key[s] > best ? key[s] : best;
+      best = wave_max_u64(best);
+      const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
+      const int owner = e & (kWave - 1);
+      const int slot = e / kWave;
+      float pe = 0.0f;
+#pragma unroll
+      for (int s = 0; s < VPL; ++s) {
+        if (s == slot) {
+          pe = p[s];
+          if (lane == owner) key[s] = 0ull;
+        }
+      }
+      pe = __shfl(pe, owner, kWave);
+      if (lane == j) {
+        my_idx = e;
+        my_gate = pe;
+      }
+    }
+    if (lane < k) {
+      idx_out[t * k + lane] = my_idx;
+      gate_out[t * k + lane] = my_gate;
+      atomicAdd(&s_hist[my_idx], 1);
+    }
+  }
+  __syncthreads();
+  int32_t *hrow = blockhist + static_cast<int64_t>(blockIdx.x) * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hrow[e] = s_hist[e];
+}
+
+// Column scan of blockhist: per expert, replace each block's count by the
+// exclusive prefix over earlier blocks and write the total to counts[e].
+// Block = 16 waves over 64 experts; wave w owns a contiguous run of blocks.
+__global__ void __launch_bounds__(1024) hist_scan_kernel(int32_t *__restrict__ blockhist,
+                                                         int nblk, int E,
+                                                         int32_t *__restrict__ counts) {
+  __shared__ int s_part[16][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int e = blockIdx.x * kWave + lane;
+  const int per = (nblk + 15) / 16;
+  const int b0 = wave * per;
+  const int b1 = min(nblk, b0 + per);
+  int sum = 0;
+  if (e < E) {
+    for (int b = b0; b < b1; ++b) sum += blockhist[static_cast<int64_t>(b) * E + e];
+  }
+  s_part[wave][lane] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int w = 0; w < wave; ++w) run += s_part[w][lane];
+  if (e < E) {
+    for (int b = b0; b < b1; ++b) {
+      int64_t o = static_cast<int64_t>(b) * E + e;
+      int c = blockhist[o];
+      blockhist[o] = run;
+      run += c;
+    }
+    if (wave == 15) counts[e] = run;
+  }
+}
+
+// Exclusive scan of a per-thread value over a 1024-thread block.
+__device__ int block_exclusive_scan(int v, int *s_tmp /* [16] */, int *total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int n = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += n;
+  }
+  if (lane == kWave - 1) s_tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < 16; ++w) {
+    int x = s_tmp[w];
+    if (w < wave) before += x;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+// Offsets of the FFN experts in permuted row order, and the prefix of GEMM
+// chunks (ceil(M_e / chunk_rows) per expert).  Single block.
+__global__ void __launch_bounds__(1024) expert_scan_kernel(const int32_t *__restrict__ counts,
+                                                           int N, int chunk_rows,
+                                                           int32_t *__restrict__ offs,
+                                                           int32_t *__restrict__ chunk_off,
+                                                           int32_t *__restrict__ meta) {
+  __shared__ int s_tmp[16];
+  int base_rows = 0, base_chunks = 0;
+  for (int e0 = 0; e0 < N; e0 += 1024) {
+    int e = e0 + threadIdx.x;
+    int c = e < N ? counts[e] : 0;
+    int ch = (c + chunk_rows - 1) / chunk_rows;
+    int tot_r, tot_c;
+    int ex_r = block_exclusive_scan(c, s_tmp, &tot_r);
+    int ex_c = block_exclusive_scan(ch, s_tmp, &tot_c);
+    if (e < N) {
+      offs[e] = base_rows + ex_r;
+      chunk_off[e] = base_chunks + ex_c;
+    }
+    base_rows += tot_r;
+    base_chunks += tot_c;
+  }
+  if (threadIdx.x == 0) {
+    offs[N] = base_rows;
+    chunk_off[N] = base_chunks;
+    meta[0] = base_chunks;
+    meta[1] = base_rows;
+  }
+}
+
+// Stable permutation: FFN slot (t, j) -> row offs[e] + (number of earlier
+// tokens routed to e).  One wave per block of kTokPerBlk tokens; tokens are
+// walked in order, lanes are slots (the k experts of a token are distinct,
+// so the lanes never touch the same counter at once).
+__global__ void __launch_bounds__(64) permute_kernel(const int32_t *__restrict__ idx, int64_t T,
+                                                     int k, int N, int E,
+                                                     const int32_t *__restrict__ offs,
+                                                     const int32_t *__restrict__ blockhist,
+                                                     int32_t *__restrict__ rowmap,
+                                                     int32_t *__restrict__ tok) {
+  __shared__ int s_next[kMaxE];
+  __shared__ int s_idx[kTokPerBlk * kMaxK];
+  const int lane = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokPerBlk;
+  const int nt = static_cast<int>(min<int64_t>(kTokPerBlk, T - t0));
+  const int32_t *hrow = blockhist + static_cast<int64_t>(blockIdx.x) * E;
+  for (int e = lane; e < N; e += kWave) s_next[e] = offs[e] + hrow[e];
+  for (int i = lane; i < nt * k; i += kWave) s_idx[i] = idx[t0 * k + i];
+  __syncthreads();
+  for (int tt = 0; tt < nt; ++tt) {
+    if (lane < k) {
+      const int e = s_idx[tt * k + lane];
+      int r = -1;
+      if (e < N) {
+        r = s_next[e];
+        s_next[e] = r + 1;
+        tok[r] = static_cast<int32_t>(t0 + tt);
+      }
+      rowmap[(t0 + tt) * k + lane] = r;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void zero_int_kernel(int32_t *p, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_topk(const Plan &p, hipStream_t s) {
+  dim3 grid(p.nblk), block(256);
+  int vpl = (p.E + kWave - 1) / kWave;
+  if (vpl <= 4)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p.logits, p.bias, p.T, p.E, p.k, p.idx,
+                       p.gate, p.blockhist);
+  else if (vpl <= 16)
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p.logits, p.bias, p.T, p.E, p.k,
+                       p.idx, p.gate, p.blockhist);
+  else
+    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p.logits, p.bias, p.T, p.E, p.k,
+                       p.idx, p.gate, p.blockhist);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const Plan &p, hipStream_t s) {
+  hipLaunchKernelGGL(hist_scan_kernel, dim3((p.E + kWave - 1) / kWave), dim3(1024), 0, s,
+                     p.blockhist, p.nblk, p.E, p.counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.N == 0) return err;
+  hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, s, p.counts, p.N, p.nbmax * 32,
+                     p.offs, p.chunk_off, p.meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const Plan &p, hipStream_t s) {
+  hipLaunchKernelGGL(permute_kernel, dim3(p.nblk), dim3(64), 0, s, p.idx, p.T, p.k, p.N, p.E,
+                     p.offs, p.blockhist, p.rowmap, p.tok);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_counts(const Plan &p, hipStream_t s) {
+  hipLaunchKernelGGL(zero_int_kernel, dim3((p.E + 255) / 256), dim3(256), 0, s, p.counts, p.E);
+  return hipGetLastError();
+}
+
+}  // namespace moezc
