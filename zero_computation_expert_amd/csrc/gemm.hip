@@ -413,6 +413,7 @@ hipError_t launch_gate_up(const Plan &p, hipStream_t s) {
   g.meta = p.meta;
   g.out = p.h;
   g.w_expert_stride = static_cast<int64_t>(p.I) * p.d;
+  g.T = p.T;  // x rows are gathered from the whole of x
   g.K = p.d;
   g.nrows = p.I;
   g.out_ld = p.I;
