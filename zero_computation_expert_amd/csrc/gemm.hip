@@ -19,7 +19,10 @@
 //   * Within each 128-byte K-step the K order is permuted identically for A
 //     and B (lane (r, h) supplies k = h*KC/2 + q*PIECE + [0, PIECE) for piece
 //     q), which lets a lane load contiguous 64-byte runs.
-//   * Weights are prefetched two K-steps ahead (three register buffers).
+//   * Weights are prefetched three K-steps ahead and token rows four (register
+//     rings), issued in consumption order so that the in-order vector-memory
+//     counter never makes a step wait for a later step's data; MFMAs cycle
+//     over 2*NB independent accumulators.
 //   * Tiles are enumerated expert-major, row-block next, chunk fastest, and
 //     block ids are remapped so that consecutive tiles land on the same XCD
 //     (workgroups are dealt round-robin over the 8 XCDs): the row blocks of
@@ -99,7 +102,6 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t *dst, float a, float b, fl
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 constexpr int kPitch = 144;  // LDS bytes per token row: 128 data + 16 pad (conflict-free b128)
-constexpr int kStages = 3;   // weight register buffers (prefetch distance 2)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: the load reads zeros
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -119,7 +121,7 @@ template <int NB>
 struct TileState {
   __amdgpu_buffer_rsrc_t ra[2];  // weight matrices (A operand)
   __amdgpu_buffer_rsrc_t rb;     // token rows (B operand)
-  uint32_t voa[2];               // byte offset of this lane's weight row piece
+  uint32_t voa[2];               // byte offset of this lane's weight row half-step
   uint32_t vob[NB];              // byte offset of this thread's token row piece (or kOOB)
   int kpos_a;                    // K element of this lane's first A piece within a step
   int kpos_b;                    // K element of this thread's B piece within a step
@@ -127,6 +129,7 @@ struct TileState {
 };
 
 // Weights of K-step ks: 4 pieces of 16 bytes per row block, straight to VGPRs.
+// Pieces past K read zeros (out-of-range buffer offset).
 template <typename T, int NB>
 __device__ __forceinline__ void load_a(uint4 (&buf)[2][4], const TileState<NB> &st, int ks) {
   constexpr int KC = 128 / sizeof(T);
@@ -140,7 +143,8 @@ __device__ __forceinline__ void load_a(uint4 (&buf)[2][4], const TileState<NB> &
   }
 }
 
-// Token rows of K-step ks into registers (one 16-byte piece per 32 rows).
+// Token rows of K-step ks into registers (one 16-byte piece per 32 rows);
+// rows past the chunk read zeros.
 template <typename T, int NB>
 __device__ __forceinline__ void load_b(uint4 (&xr)[NB], const TileState<NB> &st, int ks) {
   constexpr int KC = 128 / sizeof(T);
@@ -157,39 +161,49 @@ __device__ __forceinline__ void store_b(char *tile, const uint4 (&xr)[NB], int b
     *reinterpret_cast<uint4 *>(tile + (brow + 32 * i) * kPitch + bp * 16) = xr[i];
 }
 
+// For each 16-byte piece: the NB token fragments from LDS, then 2 x NB
+// independent MFMAs (consecutive MFMAs never share an accumulator).
 template <typename T, int NB>
 __device__ __forceinline__ void compute(floatx16 (&acc)[2][NB], const char *tile,
                                         const uint4 (&A)[2][4], int nb_rt, int r, int h) {
+  const char *bp_lds = tile + r * kPitch + h * 64;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    if (nb < nb_rt) {
-      const char *bp_lds = tile + (nb * 32 + r) * kPitch + h * 64;
-      uint4 B[4];
+  for (int q = 0; q < 4; ++q) {
+    uint4 B[NB];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) B[q] = *reinterpret_cast<const uint4 *>(bp_lds + q * 16);
+    for (int nb = 0; nb < NB; ++nb)
+      if (nb < nb_rt) B[nb] = *reinterpret_cast<const uint4 *>(bp_lds + nb * 32 * kPitch + q * 16);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+    for (int nb = 0; nb < NB; ++nb)
+      if (nb < nb_rt)
 #pragma unroll
-        for (int a = 0; a < 2; ++a) MfmaOps<T>::piece(acc[a][nb], A[a][q], B[q]);
-    }
+        for (int a = 0; a < 2; ++a) MfmaOps<T>::piece(acc[a][nb], A[a][q], B[nb]);
   }
 }
 
-// One K-step: prefetch weights two steps ahead, multiply, stage the next
-// token tile, barrier.  S is this step's weight buffer (ks % 3).
-template <typename T, int NB, int S>
+// One K-step with a ring of NST weight buffers and two token-row buffers.
+// Issue order per step: token rows of step ks + 2, weights of step
+// ks + NST - 1; then the MFMAs of step ks (weights in ring slot S, tokens in
+// LDS tile ks & 1); then the token rows of step ks + 1 go to the other LDS
+// tile.  Token rows are issued a step before the weights that follow them,
+// so the in-order vector-memory counter lets each wait cover only data this
+// step consumes, and NST - 1 steps of weights stay in flight.
+template <typename T, int NB, int NST, int S>
 __device__ __forceinline__ void kstep(int ks, int nks, floatx16 (&acc)[2][NB],
-                                      uint4 (&abuf)[kStages][2][4], uint4 (&xr)[NB],
+                                      uint4 (&abuf)[NST][2][4], uint4 (&xr)[2][NB],
                                       const TileState<NB> &st, char (*tile)[NB * 32 * kPitch],
                                       int nb_rt, int r, int h, int brow, int bp) {
-  if (ks + 2 < nks) load_a<T, NB>(abuf[(S + 2) % kStages], st, ks + 2);
+  // Loads are unconditional: past the end of K they read zeros (their
+  // buffer offsets are out of range), and a load on every path keeps the
+  // compiler's in-order wait counts exact.
+  load_b<T, NB>(xr[S & 1], st, ks + 2);
+  load_a<T, NB>(abuf[(S + NST - 1) % NST], st, ks + NST - 1);
   compute<T, NB>(acc, tile[ks & 1], abuf[S], nb_rt, r, h);
-  if (ks + 1 < nks) store_b<NB>(tile[(ks + 1) & 1], xr, brow, bp);
-  if (ks + 2 < nks) load_b<T, NB>(xr, st, ks + 2);
+  store_b<NB>(tile[(ks + 1) & 1], xr[(S + 1) & 1], brow, bp);
   __syncthreads();
 }
 
-template <typename T, int MODE, int NB>
+template <typename T, int MODE, int NB, int NST>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   constexpr int KC = 128 / sizeof(T);     // K elements per step (128 bytes per row)
   constexpr int MT = NB * 32;             // tokens per chunk
@@ -286,8 +300,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
 
   const int nks = (K + KC - 1) / KC;
 
-  uint4 abuf[kStages][2][4];
-  uint4 xr[NB];
+  static_assert(NST % 2 == 0, "the token buffers alternate with the step parity");
+  uint4 abuf[NST][2][4];
+  uint4 xr[2][NB];
   floatx16 acc[2][NB];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -296,23 +311,30 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][nb][i] = 0.0f;
 
-  // ---- prologue: token tile 0 in LDS, weights 0 and 1 and tile 1 in flight
-  load_b<T, NB>(xr, st, 0);
-  load_a<T, NB>(abuf[0], st, 0);
-  if (nks > 1) load_a<T, NB>(abuf[1], st, 1);
-  store_b<NB>(s_tile[0], xr, brow, bp);
-  if (nks > 1) load_b<T, NB>(xr, st, 1);
+  // ---- prologue: token tile 0 in LDS; then, in consumption order, token
+  // rows of step 1 and weights of steps 0 .. NST-2 ------------------------
+  load_b<T, NB>(xr[0], st, 0);
+  store_b<NB>(s_tile[0], xr[0], brow, bp);
+  load_b<T, NB>(xr[1], st, 1);
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j) load_a<T, NB>(abuf[j], st, j);
   __syncthreads();
 
-  // ---- main loop, unrolled by the three weight buffers --------------------
+  // ---- main loop, unrolled by the weight ring ----------------------------
   int ks = 0;
-  for (; ks + kStages <= nks; ks += kStages) {
-    kstep<T, NB, 0>(ks, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    kstep<T, NB, 1>(ks + 1, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    kstep<T, NB, 2>(ks + 2, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
+  for (; ks + NST <= nks; ks += NST) {
+    kstep<T, NB, NST, 0>(ks, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
+    kstep<T, NB, NST, 1>(ks + 1, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
+    if constexpr (NST > 2) {
+      kstep<T, NB, NST, 2>(ks + 2, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
+      kstep<T, NB, NST, 3>(ks + 3, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
+    }
   }
-  if (ks < nks) kstep<T, NB, 0>(ks, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
-  if (ks + 1 < nks) kstep<T, NB, 1>(ks + 1, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
+  if (ks < nks) kstep<T, NB, NST, 0>(ks, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
+  if constexpr (NST > 2) {
+    if (ks + 1 < nks) kstep<T, NB, NST, 1>(ks + 1, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
+    if (ks + 2 < nks) kstep<T, NB, NST, 2>(ks + 2, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
+  }
 
   // ---- epilogue ----------------------------------------------------------
   // Lane (r, h) holds, for column r of each 32x32 tile, rows
@@ -361,16 +383,23 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   }
 }
 
+#ifndef MOEZC_NST_BIG
+#define MOEZC_NST_BIG 4
+#endif
+#ifndef MOEZC_NST_SMALL
+#define MOEZC_NST_SMALL 4
+#endif
+
 template <typename T, int MODE>
 static hipError_t launch_gemm_t(const GemmArgs &g, int nb, int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const int64_t grid = ((max_tiles + 7) / 8) * 8;
-  if (nb == 4)
-    hipLaunchKernelGGL((gemm_kernel<T, MODE, 4>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                       s, g);
-  else
-    hipLaunchKernelGGL((gemm_kernel<T, MODE, 1>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                       s, g);
+  const dim3 gd(static_cast<unsigned>(grid)), bd(256);
+  switch (nb) {
+    case 4: hipLaunchKernelGGL((gemm_kernel<T, MODE, 4, MOEZC_NST_BIG>), gd, bd, 0, s, g); break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<T, MODE, 2, MOEZC_NST_BIG>), gd, bd, 0, s, g); break;
+    default: hipLaunchKernelGGL((gemm_kernel<T, MODE, 1, MOEZC_NST_SMALL>), gd, bd, 0, s, g); break;
+  }
   return hipGetLastError();
 }
 

@@ -147,7 +147,10 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   // many rows on average, else 32 (decode-shaped: weight streaming with few
   // rows per expert wants occupancy, not tall tiles).
   const int64_t avg_rows = dm->N > 0 ? p.pmax / dm->N : 0;
-  p.nbmax = avg_rows >= 48 ? 4 : 1;
+#ifndef MOEZC_NB_BIG
+#define MOEZC_NB_BIG 4
+#endif
+  p.nbmax = avg_rows >= 48 ? MOEZC_NB_BIG : 1;
   p.x = x;
   p.w_router = w_router;
   p.w_gate = w_gate;
