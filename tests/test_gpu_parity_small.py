@@ -57,11 +57,9 @@ def full_check(cfg, inp, bias=None, poison=False):
     P.check_counts_against_oracle(cfg, idx, cnt, oidx, omargin)
     ref = P.reference_outputs(cfg, inp, idx, oprobs)
     got = P.out_as_f32(out, cfg.dtype)
-    assert np.isfinite(got).all()
-    err = P.rel_frob(got, ref)
-    print(f"[parity] rel_frob={err:.3e} gate_err={info['gate_err']:.2e} "
+    err, worst = P.check_outputs(got, ref, cfg.dtype)
+    print(f"[parity] rel_frob={err:.3e} worst_token={worst:.3e} gate_err={info['gate_err']:.2e} "
           f"near_ties={info['near_ties']}", flush=True)
-    assert err <= P.OUT_TOL[cfg.dtype]
     return out, cnt, idx, gate
 
 

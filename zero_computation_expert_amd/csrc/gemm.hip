@@ -8,21 +8,28 @@
 // the SwiGLU form with three matrices is this library's reading of it).
 //
 // Design (weight-stationary, one pass over every weight byte):
-//   * A workgroup (4 waves) owns a block of weight rows of one expert and one
-//     chunk of up to 32*NB of that expert's tokens.  Weight rows are the MFMA
-//     "A" operand and are streamed from HBM straight into VGPRs, each lane
-//     reading 64 contiguous bytes of its row per K-step; every weight byte is
-//     used by exactly one wave, so weights never pass through LDS.
+//   * A workgroup of 4 waves owns 256 weight rows of one expert (GATE_UP: 128
+//     rows of W_gate and the same 128 rows of W_up) and one chunk of up to
+//     32*NB of that expert's tokens.  Each wave owns two 32-row blocks (the
+//     MFMA "A" operand; in GATE_UP a gate block and the up block of the same
+//     rows, so silu(g) * u is formed in registers).
+//   * Weights stream from HBM straight into LDS with direct-to-LDS buffer
+//     loads: every instruction moves 8 whole rows x 128 bytes, fully
+//     coalesced, into a three-slot ring private to the wave (two K-steps in
+//     flight without holding registers).  An XOR swizzle of the 16-byte
+//     chunks, applied on the global side, makes the MFMA-layout LDS reads
+//     bank-conflict free.  Every weight byte is read once.
 //   * Token rows (the MFMA "B" operand, shared by the 4 waves) are gathered
-//     (GATE_UP: through the token index of each permuted row) into a
-//     double-buffered LDS tile, 128 bytes of K per row per step.
+//     (GATE_UP: through the token index of each permuted row) into registers
+//     and then into a double-buffered LDS tile, 128 bytes of K per row per
+//     K-step; only this tile needs a workgroup barrier, which waits for LDS
+//     stores alone, never for the weight loads in flight.
 //   * Within each 128-byte K-step the K order is permuted identically for A
 //     and B (lane (r, h) supplies k = h*KC/2 + q*PIECE + [0, PIECE) for piece
-//     q), which lets a lane load contiguous 64-byte runs.
-//   * Weights are prefetched three K-steps ahead and token rows four (register
-//     rings), issued in consumption order so that the in-order vector-memory
-//     counter never makes a step wait for a later step's data; MFMAs cycle
-//     over 2*NB independent accumulators.
+//     q), so both operands are read as contiguous 16-byte pieces.
+//   * Loads are issued unconditionally (out-of-range buffer offsets read
+//     zeros) and in consumption order, so the in-order vector-memory counter
+//     never makes a step wait for data of a later step.
 //   * Tiles are enumerated expert-major, row-block next, chunk fastest, and
 //     block ids are remapped so that consecutive tiles land on the same XCD
 //     (workgroups are dealt round-robin over the 8 XCDs): the row blocks of
@@ -37,6 +44,8 @@ namespace moezc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 enum { MODE_ROUTER = 0, MODE_GATE_UP = 1, MODE_DOWN = 2 };
 
@@ -50,7 +59,7 @@ struct GemmArgs {
   const int32_t *meta;       // meta[0] = total chunks (GATE_UP, DOWN)
   void *out;                 // logits (f32) / H / Y
   int64_t w_expert_stride;   // elements between experts' matrices
-  int64_t T;                 // ROUTER: tokens
+  int64_t T;                 // tokens (ROUTER: chunking; GATE_UP: rows of x)
   int K;                     // reduction length
   int nrows;                 // weight rows per expert (E, I or d)
   int out_ld;                // elements per output row
@@ -101,10 +110,11 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t *dst, float a, float b, fl
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
+constexpr int kThreads = 256;                  // 4 waves, each with two 32-row weight blocks
+constexpr int kWaveRowBytes = 64 * 128;        // one K-step of a wave's 64 weight rows
+constexpr int kWSlotBytes = 4 * kWaveRowBytes; // one K-step of the workgroup's weights
 constexpr int kPitch = 144;  // LDS bytes per token row: 128 data + 16 pad (conflict-free b128)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: the load reads zeros
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
@@ -119,32 +129,44 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t rs, uint32_t off) 
 // Per-thread state of one tile.
 template <int NB>
 struct TileState {
-  __amdgpu_buffer_rsrc_t ra[2];  // weight matrices (A operand)
+  __amdgpu_buffer_rsrc_t ra[2];  // weight matrix of each 32-row block (A operand)
   __amdgpu_buffer_rsrc_t rb;     // token rows (B operand)
-  uint32_t voa[2];               // byte offset of this lane's weight row half-step
+  uint32_t wrow[2][4];           // byte offset of the weight row this lane loads in each
+                                 // direct-to-LDS instruction (block, 8-row group)
+  uint32_t wchunk;               // byte offset of the 16-byte chunk this lane loads
+  int wkpos;                     // K element of that chunk within a step
   uint32_t vob[NB];              // byte offset of this thread's token row piece (or kOOB)
-  int kpos_a;                    // K element of this lane's first A piece within a step
-  int kpos_b;                    // K element of this thread's B piece within a step
+  int kpos_b;                    // K element of this thread's token piece within a step
   int K;
 };
 
-// Weights of K-step ks: 4 pieces of 16 bytes per row block, straight to VGPRs.
-// Pieces past K read zeros (out-of-range buffer offset).
+// Weights of K-step ks from HBM into this wave's LDS slot: 8 fully
+// coalesced instructions of 8 rows x 128 bytes.  Lane l of instruction i
+// loads row (i%4)*8 + l/8 of block i/4 and lands in LDS chunk l%8, which
+// therefore holds the row's 16-byte chunk (l%8) ^ (l/8) (XOR swizzle).
+// Chunks past K read zeros.
 template <typename T, int NB>
-__device__ __forceinline__ void load_a(uint4 (&buf)[2][4], const TileState<NB> &st, int ks) {
+__device__ __forceinline__ void load_w(char *slot_wave, const TileState<NB> &st, int ks) {
   constexpr int KC = 128 / sizeof(T);
-  constexpr int PIECE = 16 / sizeof(T);
+  const bool ok = ks * KC + st.wkpos < st.K;
+  const uint32_t o = ks * 128 + st.wchunk;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const bool ok = ks * KC + st.kpos_a + q * PIECE < st.K;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-      buf[a][q] = bload(st.ra[a], ok ? st.voa[a] + ks * 128 + q * 16 : kOOB);
+  for (int i = 0; i < 8; ++i) {
+    const int a = i >> 2;
+#if defined(__HIP_DEVICE_COMPILE__)  // the direct-to-LDS load exists only for the device
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        st.ra[a], (lds_void *)(slot_wave + (a * 32 + (i & 3) * 8) * 128), 16,
+        ok ? st.wrow[a][i & 3] + o : kOOB, 0, 0, 0);
+#else
+    (void)a;
+    (void)o;
+    (void)ok;
+#endif
   }
 }
 
-// Token rows of K-step ks into registers (one 16-byte piece per 32 rows);
-// rows past the chunk read zeros.
+// Token rows of K-step ks into registers; rows past the chunk and pieces
+// past K read zeros.
 template <typename T, int NB>
 __device__ __forceinline__ void load_b(uint4 (&xr)[NB], const TileState<NB> &st, int ks) {
   constexpr int KC = 128 / sizeof(T);
@@ -161,54 +183,93 @@ __device__ __forceinline__ void store_b(char *tile, const uint4 (&xr)[NB], int b
     *reinterpret_cast<uint4 *>(tile + (brow + 32 * i) * kPitch + bp * 16) = xr[i];
 }
 
-// For each 16-byte piece: the NB token fragments from LDS, then 2 x NB
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations are outstanding, leaving the other counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// MFMAs of one K-step: per 16-byte piece q, the wave's two weight fragments
+// (swizzled slot) and the NB token fragments (tile), then 2 x NB
 // independent MFMAs (consecutive MFMAs never share an accumulator).
+//
+// The slot was filled by the direct-to-LDS loads of two steps ago.  Each
+// such load writes 64 lanes x 16 bytes, but the compiler's dependence
+// tracking sees only the 16 bytes at its base address, so it would let some
+// slot reads pass the fill.  The wait is therefore explicit: every step
+// (and each of the two prologue groups) issues NB token loads and 8 weight
+// loads, and compiler-level barriers keep the groups in order, so at most
+// 2 * (NB + 8) younger operations may remain outstanding.  The empty asm
+// keeps the slot reads below the wait.
 template <typename T, int NB>
-__device__ __forceinline__ void compute(floatx16 (&acc)[2][NB], const char *tile,
-                                        const uint4 (&A)[2][4], int nb_rt, int r, int h) {
-  const char *bp_lds = tile + r * kPitch + h * 64;
+__device__ __forceinline__ void compute(floatx16 (&acc)[2][NB], const char *slot_wave,
+                                        const char *tile, int nb_rt, int r, int h) {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (NB + 8)));
+  asm volatile("" ::: "memory");
+  const char *tb = tile + r * kPitch + h * 64;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    uint4 B[NB];
+    const int chunk = ((h * 4 + q) ^ (r & 7)) * 16;
+    uint4 A[2], B[NB];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+      A[a] = *reinterpret_cast<const uint4 *>(slot_wave + (a * 32 + r) * 128 + chunk);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      if (nb < nb_rt) B[nb] = *reinterpret_cast<const uint4 *>(bp_lds + nb * 32 * kPitch + q * 16);
+      if (nb < nb_rt) B[nb] = *reinterpret_cast<const uint4 *>(tb + nb * 32 * kPitch + q * 16);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       if (nb < nb_rt)
 #pragma unroll
-        for (int a = 0; a < 2; ++a) MfmaOps<T>::piece(acc[a][nb], A[a][q], B[nb]);
+        for (int a = 0; a < 2; ++a) MfmaOps<T>::piece(acc[a][nb], A[a], B[nb]);
   }
 }
 
-// One K-step with a ring of NST weight buffers and two token-row buffers.
-// Issue order per step: token rows of step ks + 2, weights of step
-// ks + NST - 1; then the MFMAs of step ks (weights in ring slot S, tokens in
-// LDS tile ks & 1); then the token rows of step ks + 1 go to the other LDS
-// tile.  Token rows are issued a step before the weights that follow them,
-// so the in-order vector-memory counter lets each wait cover only data this
-// step consumes, and NST - 1 steps of weights stay in flight.
-template <typename T, int NB, int NST, int S>
-__device__ __forceinline__ void kstep(int ks, int nks, floatx16 (&acc)[2][NB],
-                                      uint4 (&abuf)[NST][2][4], uint4 (&xr)[2][NB],
-                                      const TileState<NB> &st, char (*tile)[NB * 32 * kPitch],
-                                      int nb_rt, int r, int h, int brow, int bp) {
-  // Loads are unconditional: past the end of K they read zeros (their
-  // buffer offsets are out of range), and a load on every path keeps the
-  // compiler's in-order wait counts exact.
-  load_b<T, NB>(xr[S & 1], st, ks + 2);
-  load_a<T, NB>(abuf[(S + NST - 1) % NST], st, ks + NST - 1);
-  compute<T, NB>(acc, tile[ks & 1], abuf[S], nb_rt, r, h);
-  store_b<NB>(tile[(ks + 1) & 1], xr[(S + 1) & 1], brow, bp);
-  __syncthreads();
+// Workgroup barrier for the token tile.  The tile is written with ordinary
+// LDS stores, so waiting for the LDS counter suffices; the weight slots are
+// private to each wave and their direct-to-LDS loads stay in flight across
+// the barrier (a full fence would wait for them).  The empty asm statements
+// keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-template <typename T, int MODE, int NB, int NST>
-__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
+template <int NB>
+using TileBuf = char[NB * 32 * kPitch];
+
+// One K-step (S = ks mod 6 selects the weight slot ks mod 3 and the token
+// buffer ks mod 2 at compile time): token rows of step ks + 2 are issued
+// before the weights of step ks + 2 (so waiting for them never waits for the
+// weights), the weights go to the slot read in step ks - 1, then the MFMAs
+// of step ks, the token rows of step ks + 1 into the other tile, and the
+// barrier.
+template <typename T, int NB, int S>
+__device__ __forceinline__ void kstep(int ks, floatx16 (&acc)[2][NB], char *w0, char *w1,
+                                      char *w2, uint4 (&xr)[2][NB], const TileState<NB> &st,
+                                      TileBuf<NB> *tile, int nb_rt, int r, int h, int brow,
+                                      int bp) {
+  char *const slot_now = S % 3 == 0 ? w0 : (S % 3 == 1 ? w1 : w2);
+  char *const slot_next = (S + 2) % 3 == 0 ? w0 : ((S + 2) % 3 == 1 ? w1 : w2);
+  load_b<T, NB>(xr[S & 1], st, ks + 2);
+  load_w<T, NB>(slot_next, st, ks + 2);
+  compute<T, NB>(acc, slot_now, tile[ks & 1], nb_rt, r, h);
+  store_b<NB>(tile[(ks + 1) & 1], xr[(S + 1) & 1], brow, bp);
+  tile_barrier();
+}
+
+template <typename T, int MODE, int NB>
+__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
   constexpr int KC = 128 / sizeof(T);     // K elements per step (128 bytes per row)
   constexpr int MT = NB * 32;             // tokens per chunk
   constexpr uint32_t ES = sizeof(T);
-  __shared__ __attribute__((aligned(16))) char s_tile[2][MT * kPitch];
+  // Three weight slots as distinct LDS objects: the compiler tracks the
+  // direct-to-LDS loads of each separately, so a read of one slot waits only
+  // for the loads into that slot.
+  __shared__ __attribute__((aligned(16))) char s_w0[kWSlotBytes];
+  __shared__ __attribute__((aligned(16))) char s_w1[kWSlotBytes];
+  __shared__ __attribute__((aligned(16))) char s_w2[kWSlotBytes];
+  __shared__ __attribute__((aligned(16))) TileBuf<NB> s_tile[2];
   __shared__ int s_co[kMaxE + 1];
 
   // ---- which tile -------------------------------------------------------
@@ -259,25 +320,29 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
 
   TileState<NB> st;
   st.K = K;
-  st.kpos_a = h * (KC / 2);
-  // ---- weight rows of this lane (MFMA A operand) -------------------------
+  // ---- the 64 weight rows of this wave (MFMA A operand) -------------------
   const uint32_t wbytes = static_cast<uint32_t>(g.nrows) * static_cast<uint32_t>(K) * ES;
-  const char *w0 = static_cast<const char *>(g.wa) + e * g.w_expert_stride * ES;
-  int rowbase;  // first weight row of this wave
+  int rowbase[2];  // first weight row of each 32-row block
   if (MODE == MODE_GATE_UP) {
-    rowbase = rb * 128 + wave * 32;
-    const int row = min(rowbase + r, g.nrows - 1);
-    st.ra[0] = make_rsrc(w0, wbytes);
+    rowbase[0] = rowbase[1] = rb * 128 + wave * 32;  // block 0: W_gate, block 1: W_up
+    st.ra[0] = make_rsrc(static_cast<const char *>(g.wa) + e * g.w_expert_stride * ES, wbytes);
     st.ra[1] = make_rsrc(static_cast<const char *>(g.wb) + e * g.w_expert_stride * ES, wbytes);
-    st.voa[0] = st.voa[1] = static_cast<uint32_t>(row) * K * ES + h * 64;
   } else {
-    rowbase = rb * 256 + wave * 64;
-    st.ra[0] = st.ra[1] = make_rsrc(w0, wbytes);
+    rowbase[0] = rb * 256 + wave * 64;
+    rowbase[1] = rowbase[0] + 32;
+    st.ra[0] = st.ra[1] =
+        make_rsrc(static_cast<const char *>(g.wa) + e * g.w_expert_stride * ES, wbytes);
+  }
+  {
+    const int lr = lane >> 3;           // row within an 8-row group
+    const int chunk = (lane & 7) ^ lr;  // logical 16-byte chunk this lane loads
+    st.wchunk = chunk * 16;
+    st.wkpos = chunk * (16 / static_cast<int>(ES));
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int row = min(rowbase + a * 32 + r, g.nrows - 1);
-      st.voa[a] = static_cast<uint32_t>(row) * K * ES + h * 64;
-    }
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        st.wrow[a][j] = static_cast<uint32_t>(min(rowbase[a] + j * 8 + lr, g.nrows - 1)) * K * ES;
   }
 
   // ---- token rows this thread stages into LDS (B operand) ----------------
@@ -299,9 +364,10 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   }
 
   const int nks = (K + KC - 1) / KC;
+  char *const w0 = s_w0 + wave * kWaveRowBytes;
+  char *const w1 = s_w1 + wave * kWaveRowBytes;
+  char *const w2 = s_w2 + wave * kWaveRowBytes;
 
-  static_assert(NST % 2 == 0, "the token buffers alternate with the step parity");
-  uint4 abuf[NST][2][4];
   uint4 xr[2][NB];
   floatx16 acc[2][NB];
 #pragma unroll
@@ -311,30 +377,38 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][nb][i] = 0.0f;
 
-  // ---- prologue: token tile 0 in LDS; then, in consumption order, token
-  // rows of step 1 and weights of steps 0 .. NST-2 ------------------------
+  // ---- prologue: the loads of steps 0 and 1 in the same per-step groups
+  // as the main loop (token rows, then weights), which the explicit wait in
+  // compute() counts on; token tile 0 goes to LDS in between --------------
   load_b<T, NB>(xr[0], st, 0);
+  load_w<T, NB>(w0, st, 0);
+  asm volatile("" ::: "memory");  // keep the step-0 group ahead of the rest
   store_b<NB>(s_tile[0], xr[0], brow, bp);
   load_b<T, NB>(xr[1], st, 1);
-#pragma unroll
-  for (int j = 0; j < NST - 1; ++j) load_a<T, NB>(abuf[j], st, j);
-  __syncthreads();
+  load_w<T, NB>(w1, st, 1);
+  tile_barrier();
 
-  // ---- main loop, unrolled by the weight ring ----------------------------
+  // ---- main loop, unrolled by lcm(3 weight slots, 2 token buffers) --------
   int ks = 0;
-  for (; ks + NST <= nks; ks += NST) {
-    kstep<T, NB, NST, 0>(ks, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    kstep<T, NB, NST, 1>(ks + 1, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    if constexpr (NST > 2) {
-      kstep<T, NB, NST, 2>(ks + 2, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
-      kstep<T, NB, NST, 3>(ks + 3, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    }
+  for (; ks + 6 <= nks; ks += 6) {
+    kstep<T, NB, 0>(ks, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+    kstep<T, NB, 1>(ks + 1, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+    kstep<T, NB, 2>(ks + 2, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+    kstep<T, NB, 3>(ks + 3, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+    kstep<T, NB, 4>(ks + 4, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+    kstep<T, NB, 5>(ks + 5, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
   }
-  if (ks < nks) kstep<T, NB, NST, 0>(ks, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
-  if constexpr (NST > 2) {
-    if (ks + 1 < nks) kstep<T, NB, NST, 1>(ks + 1, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    if (ks + 2 < nks) kstep<T, NB, NST, 2>(ks + 2, nks, acc, abuf, xr, st, s_tile, nb_rt, r, h, brow, bp);
-  }
+  if (ks < nks) kstep<T, NB, 0>(ks, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+  if (ks + 1 < nks) kstep<T, NB, 1>(ks + 1, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+  if (ks + 2 < nks) kstep<T, NB, 2>(ks + 2, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+  if (ks + 3 < nks) kstep<T, NB, 3>(ks + 3, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+  if (ks + 4 < nks) kstep<T, NB, 4>(ks + 4, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+
+  // Drain the prefetches past the end of K (they read zeros into slots that
+  // are never read) so that no direct-to-LDS write is still in flight when
+  // the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" ::: "memory");
 
   // ---- epilogue ----------------------------------------------------------
   // Lane (r, h) holds, for column r of each 32x32 tile, rows
@@ -351,14 +425,14 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
         for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int row = rowbase + a * 32 + gi * 8 + h * 4 + j;
+            const int row = rowbase[a] + gi * 8 + h * 4 + j;
             if (row < g.nrows) orow[row] = acc[a][nb][gi * 4 + j];
           }
     } else if (MODE == MODE_GATE_UP) {
       T *orow = static_cast<T *>(g.out) + (static_cast<int64_t>(m0) + col) * g.out_ld;
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
-        const int row = rowbase + gi * 8 + h * 4;
+        const int row = rowbase[0] + gi * 8 + h * 4;
         if (row < g.nrows) {
           const floatx16 &ga = acc[0][nb];
           const floatx16 &ua = acc[1][nb];
@@ -374,7 +448,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
-          const int row = rowbase + a * 32 + gi * 8 + h * 4;
+          const int row = rowbase[a] + gi * 8 + h * 4;
           if (row < g.nrows)
             store4<T>(orow + row, acc[a][nb][gi * 4 + 0], acc[a][nb][gi * 4 + 1],
                       acc[a][nb][gi * 4 + 2], acc[a][nb][gi * 4 + 3]);
@@ -383,23 +457,18 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   }
 }
 
-#ifndef MOEZC_NST_BIG
-#define MOEZC_NST_BIG 4
-#endif
-#ifndef MOEZC_NST_SMALL
-#define MOEZC_NST_SMALL 4
-#endif
+// Weight rows one workgroup covers (GATE_UP: per matrix).
+static int rows_per_wg(int mode) { return mode == MODE_GATE_UP ? 128 : 256; }
 
 template <typename T, int MODE>
 static hipError_t launch_gemm_t(const GemmArgs &g, int nb, int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const int64_t grid = ((max_tiles + 7) / 8) * 8;
-  const dim3 gd(static_cast<unsigned>(grid)), bd(256);
-  switch (nb) {
-    case 4: hipLaunchKernelGGL((gemm_kernel<T, MODE, 4, MOEZC_NST_BIG>), gd, bd, 0, s, g); break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<T, MODE, 2, MOEZC_NST_BIG>), gd, bd, 0, s, g); break;
-    default: hipLaunchKernelGGL((gemm_kernel<T, MODE, 1, MOEZC_NST_SMALL>), gd, bd, 0, s, g); break;
-  }
+  const dim3 gd(static_cast<unsigned>(grid)), bd(kThreads);
+  if (nb == 4)
+    hipLaunchKernelGGL((gemm_kernel<T, MODE, 4>), gd, bd, 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, MODE, 1>), gd, bd, 0, s, g);
   return hipGetLastError();
 }
 
@@ -425,7 +494,7 @@ hipError_t launch_router_gemm(const Plan &p, hipStream_t s) {
   g.K = p.d;
   g.nrows = p.E;
   g.out_ld = p.E;
-  g.nrb = (p.E + 255) / 256;
+  g.nrb = (p.E + rows_per_wg(MODE_ROUTER) - 1) / rows_per_wg(MODE_ROUTER);
   const int nb = 4;
   const int64_t tiles = ((p.T + 32 * nb - 1) / (32 * nb)) * g.nrb;
   return launch_gemm<MODE_ROUTER>(p, g, nb, tiles, s);
@@ -446,7 +515,7 @@ hipError_t launch_gate_up(const Plan &p, hipStream_t s) {
   g.K = p.d;
   g.nrows = p.I;
   g.out_ld = p.I;
-  g.nrb = (p.I + 127) / 128;
+  g.nrb = (p.I + rows_per_wg(MODE_GATE_UP) - 1) / rows_per_wg(MODE_GATE_UP);
   g.N = p.N;
   return launch_gemm<MODE_GATE_UP>(p, g, p.nbmax, max_chunks(p) * g.nrb, s);
 }
@@ -463,7 +532,7 @@ hipError_t launch_down(const Plan &p, hipStream_t s) {
   g.K = p.I;
   g.nrows = p.d;
   g.out_ld = p.d;
-  g.nrb = (p.d + 255) / 256;
+  g.nrb = (p.d + rows_per_wg(MODE_DOWN) - 1) / rows_per_wg(MODE_DOWN);
   g.N = p.N;
   return launch_gemm<MODE_DOWN>(p, g, p.nbmax, max_chunks(p) * g.nrb, s);
 }
