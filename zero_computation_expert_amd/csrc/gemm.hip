@@ -10,9 +10,12 @@
 // Design (weight-stationary, one pass over every weight byte):
 //   * A workgroup of 4 waves owns 256 weight rows of one expert (GATE_UP: 128
 //     rows of W_gate and the same 128 rows of W_up) and one chunk of up to
-//     32*NB of that expert's tokens.  Each wave owns two 32-row blocks (the
-//     MFMA "A" operand; in GATE_UP a gate block and the up block of the same
-//     rows, so silu(g) * u is formed in registers).
+//     32*NB of that expert's tokens (NB = 8: 256 tokens, so that an expert
+//     with up to 256 tokens streams its weights exactly once).  Each wave owns
+//     two 32-row blocks (the MFMA "A" operand; in GATE_UP a gate block and the
+//     up block of the same rows, so silu(g) * u is formed in registers) against
+//     all the chunk's token blocks; at NB = 8 its 256 accumulators per lane
+//     take half of the unified register file, which one wave per SIMD owns.
 //   * Weights stream from HBM straight into LDS with direct-to-LDS buffer
 //     loads: every instruction moves 8 whole rows x 128 bytes, fully
 //     coalesced, into a three-slot ring private to the wave (two K-steps in
@@ -22,8 +25,10 @@
 //   * Token rows (the MFMA "B" operand, shared by the 4 waves) are gathered
 //     (GATE_UP: through the token index of each permuted row) into registers
 //     and then into a double-buffered LDS tile, 128 bytes of K per row per
-//     K-step; only this tile needs a workgroup barrier, which waits for LDS
-//     stores alone, never for the weight loads in flight.
+//     K-step, with the same XOR swizzle as the weights (no padding: three
+//     weight slots and two 256-row tiles fill the 160 KB of LDS); only this
+//     tile needs a workgroup barrier, which waits for LDS stores alone, never
+//     for the weight loads in flight.
 //   * Within each 128-byte K-step the K order is permuted identically for A
 //     and B (lane (r, h) supplies k = h*KC/2 + q*PIECE + [0, PIECE) for piece
 //     q), so both operands are read as contiguous 16-byte pieces.
@@ -113,7 +118,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 constexpr int kThreads = 256;                  // 4 waves, each with two 32-row weight blocks
 constexpr int kWaveRowBytes = 64 * 128;        // one K-step of a wave's 64 weight rows
 constexpr int kWSlotBytes = 4 * kWaveRowBytes; // one K-step of the workgroup's weights
-constexpr int kPitch = 144;  // LDS bytes per token row: 128 data + 16 pad (conflict-free b128)
+constexpr int kPitch = 128;  // LDS bytes per token row (16-byte chunks XOR-swizzled by row)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: the load reads zeros
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -176,50 +181,69 @@ __device__ __forceinline__ void load_b(uint4 (&xr)[NB], const TileState<NB> &st,
     xr[i] = bload(st.rb, (ok && st.vob[i] != kOOB) ? st.vob[i] + ks * 128 : kOOB);
 }
 
+// Token piece bp of tile row brow + 32 i lands in chunk bp ^ (brow & 7) of
+// that row (the row's low 3 bits are brow's: 32 i is a multiple of 8).
 template <int NB>
 __device__ __forceinline__ void store_b(char *tile, const uint4 (&xr)[NB], int brow, int bp) {
+  const int chunk = (bp ^ (brow & 7)) * 16;
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    *reinterpret_cast<uint4 *>(tile + (brow + 32 * i) * kPitch + bp * 16) = xr[i];
+    *reinterpret_cast<uint4 *>(tile + (brow + 32 * i) * kPitch + chunk) = xr[i];
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
 // memory operations are outstanding, leaving the other counters alone.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// MFMAs of one K-step: per 16-byte piece q, the wave's two weight fragments
-// (swizzled slot) and the NB token fragments (tile), then 2 x NB
-// independent MFMAs (consecutive MFMAs never share an accumulator).
+// MFMAs of one K-step: per 16-byte piece q, 2 x NBR independent MFMAs
+// (consecutive MFMAs never share an accumulator) over the wave's two weight
+// fragments and the NBR live token fragments.
+// NBR is a compile-time count (the tile is dispatched on it once), so the
+// step is straight-line code the compiler can software-pipeline.
 //
 // The slot was filled by the direct-to-LDS loads of two steps ago.  Each
 // such load writes 64 lanes x 16 bytes, but the compiler's dependence
 // tracking sees only the 16 bytes at its base address, so it would let some
 // slot reads pass the fill.  The wait is therefore explicit: every step
-// (and each of the two prologue groups) issues NB token loads and 8 weight
+// (and each of the two prologue groups) issues NBR token loads and 8 weight
 // loads, and compiler-level barriers keep the groups in order, so at most
-// 2 * (NB + 8) younger operations may remain outstanding.  The empty asm
+// 2 * (NBR + 8) younger operations may remain outstanding.  The empty asm
 // keeps the slot reads below the wait.
-template <typename T, int NB>
-__device__ __forceinline__ void compute(floatx16 (&acc)[2][NB], const char *slot_wave,
-                                        const char *tile, int nb_rt, int r, int h) {
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (NB + 8)));
+// Fragments of 16-byte piece q: the wave's two weight fragments (swizzled
+// slot) and the NBR token fragments (swizzled tile); both operands hold
+// logical chunk h*4 + q of a row whose low 3 bits are r's.
+template <int NBR>
+__device__ __forceinline__ void load_frags(uint4 (&A)[2], uint4 (&B)[NBR], const char *slot_wave,
+                                           const char *tb, int r, int h, int q) {
+  const int chunk = ((h * 4 + q) ^ (r & 7)) * 16;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+    A[a] = *reinterpret_cast<const uint4 *>(slot_wave + (a * 32 + r) * 128 + chunk);
+#pragma unroll
+  for (int nb = 0; nb < NBR; ++nb)
+    B[nb] = *reinterpret_cast<const uint4 *>(tb + nb * 32 * kPitch + chunk);
+}
+
+template <typename T, int NBR>
+__device__ __forceinline__ void compute(floatx16 (&acc)[2][NBR], const char *slot_wave,
+                                        const char *tile, int r, int h) {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (NBR + 8)));
   asm volatile("" ::: "memory");
-  const char *tb = tile + r * kPitch + h * 64;
+  const char *tb = tile + r * kPitch;
+  // The reads of piece q + 1 are issued before the MFMAs of piece q, so the
+  // LDS latency hides behind 2 x NBR MFMAs; scheduling fences keep the
+  // compiler from regrouping them (it would otherwise read just in time).
+  uint4 A[2][2], B[2][NBR];
+  load_frags<NBR>(A[0], B[0], slot_wave, tb, r, h, 0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int chunk = ((h * 4 + q) ^ (r & 7)) * 16;
-    uint4 A[2], B[NB];
+    if (q < 3) load_frags<NBR>(A[(q + 1) & 1], B[(q + 1) & 1], slot_wave, tb, r, h, q + 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-      A[a] = *reinterpret_cast<const uint4 *>(slot_wave + (a * 32 + r) * 128 + chunk);
+    for (int nb = 0; nb < NBR; ++nb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      if (nb < nb_rt) B[nb] = *reinterpret_cast<const uint4 *>(tb + nb * 32 * kPitch + q * 16);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      if (nb < nb_rt)
-#pragma unroll
-        for (int a = 0; a < 2; ++a) MfmaOps<T>::piece(acc[a][nb], A[a], B[nb]);
+      for (int a = 0; a < 2; ++a) MfmaOps<T>::piece(acc[a][nb], A[q & 1][a], B[q & 1][nb]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -244,73 +268,32 @@ using TileBuf = char[NB * 32 * kPitch];
 // weights), the weights go to the slot read in step ks - 1, then the MFMAs
 // of step ks, the token rows of step ks + 1 into the other tile, and the
 // barrier.
-template <typename T, int NB, int S>
-__device__ __forceinline__ void kstep(int ks, floatx16 (&acc)[2][NB], char *w0, char *w1,
-                                      char *w2, uint4 (&xr)[2][NB], const TileState<NB> &st,
-                                      TileBuf<NB> *tile, int nb_rt, int r, int h, int brow,
-                                      int bp) {
+template <typename T, int NB, int NBR, int S>
+__device__ __forceinline__ void kstep(int ks, floatx16 (&acc)[2][NBR], char *w0, char *w1,
+                                      char *w2, uint4 (&xr)[2][NBR], const TileState<NBR> &st,
+                                      TileBuf<NB> *tile, int r, int h, int brow, int bp) {
   char *const slot_now = S % 3 == 0 ? w0 : (S % 3 == 1 ? w1 : w2);
   char *const slot_next = (S + 2) % 3 == 0 ? w0 : ((S + 2) % 3 == 1 ? w1 : w2);
-  load_b<T, NB>(xr[S & 1], st, ks + 2);
-  load_w<T, NB>(slot_next, st, ks + 2);
-  compute<T, NB>(acc, slot_now, tile[ks & 1], nb_rt, r, h);
-  store_b<NB>(tile[(ks + 1) & 1], xr[(S + 1) & 1], brow, bp);
+  load_b<T, NBR>(xr[S & 1], st, ks + 2);
+  load_w<T, NBR>(slot_next, st, ks + 2);
+  compute<T, NBR>(acc, slot_now, tile[ks & 1], r, h);
+  store_b<NBR>(tile[(ks + 1) & 1], xr[(S + 1) & 1], brow, bp);
   tile_barrier();
 }
 
-template <typename T, int MODE, int NB>
-__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
-  constexpr int KC = 128 / sizeof(T);     // K elements per step (128 bytes per row)
-  constexpr int MT = NB * 32;             // tokens per chunk
+// Where a tile sits: expert e, weight row block rb, token rows [m0, m0 + mcount).
+struct TileLoc {
+  int e, rb, m0, mcount;
+};
+
+// The whole K loop and epilogue of one tile with NBR live 32-token blocks
+// (NBR <= NB; the LDS buffers are sized for NB).
+template <typename T, int MODE, int NB, int NBR>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t, char *s_w0,
+                                          char *s_w1, char *s_w2, TileBuf<NB> *s_tile) {
+  constexpr int KC = 128 / sizeof(T);  // K elements per step (128 bytes per row)
   constexpr uint32_t ES = sizeof(T);
-  // Three weight slots as distinct LDS objects: the compiler tracks the
-  // direct-to-LDS loads of each separately, so a read of one slot waits only
-  // for the loads into that slot.
-  __shared__ __attribute__((aligned(16))) char s_w0[kWSlotBytes];
-  __shared__ __attribute__((aligned(16))) char s_w1[kWSlotBytes];
-  __shared__ __attribute__((aligned(16))) char s_w2[kWSlotBytes];
-  __shared__ __attribute__((aligned(16))) TileBuf<NB> s_tile[2];
-  __shared__ int s_co[kMaxE + 1];
-
-  // ---- which tile -------------------------------------------------------
-  int ntiles;
-  if (MODE == MODE_ROUTER) {
-    ntiles = static_cast<int>((g.T + MT - 1) / MT) * g.nrb;
-  } else {
-    ntiles = g.meta[0] * g.nrb;
-  }
-  const int quota = (ntiles + 7) / 8;
-  const int loc = blockIdx.x / 8;
-  if (loc >= quota) return;
-  const int v = (blockIdx.x % 8) * quota + loc;
-  if (v >= ntiles) return;
-
-  int e = 0, rb, m0, mcount;
-  if (MODE == MODE_ROUTER) {
-    const int nch = static_cast<int>((g.T + MT - 1) / MT);
-    rb = v / nch;
-    const int ch = v % nch;
-    m0 = ch * MT;
-    mcount = static_cast<int>(min<int64_t>(MT, g.T - m0));
-  } else {
-    for (int i = threadIdx.x; i <= g.N; i += blockDim.x) s_co[i] = g.chunk_off[i];
-    __syncthreads();
-    const int c = v / g.nrb;
-    int lo = 0, hi = g.N - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_co[mid] <= c) lo = mid;
-      else hi = mid - 1;
-    }
-    e = lo;
-    const int local = v - g.nrb * s_co[e];
-    const int nch = s_co[e + 1] - s_co[e];
-    rb = local / nch;
-    const int ch = local - rb * nch;
-    m0 = g.offs[e] + ch * MT;
-    mcount = min(MT, g.offs[e + 1] - m0);
-  }
-  const int nb_rt = (mcount + 31) / 32;
+  const int e = t.e, rb = t.rb, m0 = t.m0, mcount = t.mcount;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -318,7 +301,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
   const int h = lane >> 5;
   const int K = g.K;
 
-  TileState<NB> st;
+  TileState<NBR> st;
   st.K = K;
   // ---- the 64 weight rows of this wave (MFMA A operand) -------------------
   const uint32_t wbytes = static_cast<uint32_t>(g.nrows) * static_cast<uint32_t>(K) * ES;
@@ -356,7 +339,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
                       static_cast<uint32_t>(mcount) * K * ES);
   }
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
+  for (int i = 0; i < NBR; ++i) {
     const int tr = brow + 32 * i;
     uint32_t row = 0;
     if (tr < mcount) row = MODE == MODE_GATE_UP ? static_cast<uint32_t>(g.tok[m0 + tr]) : tr;
@@ -368,41 +351,41 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
   char *const w1 = s_w1 + wave * kWaveRowBytes;
   char *const w2 = s_w2 + wave * kWaveRowBytes;
 
-  uint4 xr[2][NB];
-  floatx16 acc[2][NB];
+  uint4 xr[2][NBR];
+  floatx16 acc[2][NBR];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NBR; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][nb][i] = 0.0f;
 
   // ---- prologue: the loads of steps 0 and 1 in the same per-step groups
   // as the main loop (token rows, then weights), which the explicit wait in
   // compute() counts on; token tile 0 goes to LDS in between --------------
-  load_b<T, NB>(xr[0], st, 0);
-  load_w<T, NB>(w0, st, 0);
+  load_b<T, NBR>(xr[0], st, 0);
+  load_w<T, NBR>(w0, st, 0);
   asm volatile("" ::: "memory");  // keep the step-0 group ahead of the rest
-  store_b<NB>(s_tile[0], xr[0], brow, bp);
-  load_b<T, NB>(xr[1], st, 1);
-  load_w<T, NB>(w1, st, 1);
+  store_b<NBR>(s_tile[0], xr[0], brow, bp);
+  load_b<T, NBR>(xr[1], st, 1);
+  load_w<T, NBR>(w1, st, 1);
   tile_barrier();
 
   // ---- main loop, unrolled by lcm(3 weight slots, 2 token buffers) --------
   int ks = 0;
   for (; ks + 6 <= nks; ks += 6) {
-    kstep<T, NB, 0>(ks, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    kstep<T, NB, 1>(ks + 1, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    kstep<T, NB, 2>(ks + 2, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    kstep<T, NB, 3>(ks + 3, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    kstep<T, NB, 4>(ks + 4, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
-    kstep<T, NB, 5>(ks + 5, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+    kstep<T, NB, NBR, 0>(ks, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
+    kstep<T, NB, NBR, 1>(ks + 1, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
+    kstep<T, NB, NBR, 2>(ks + 2, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
+    kstep<T, NB, NBR, 3>(ks + 3, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
+    kstep<T, NB, NBR, 4>(ks + 4, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
+    kstep<T, NB, NBR, 5>(ks + 5, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
   }
-  if (ks < nks) kstep<T, NB, 0>(ks, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
-  if (ks + 1 < nks) kstep<T, NB, 1>(ks + 1, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
-  if (ks + 2 < nks) kstep<T, NB, 2>(ks + 2, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
-  if (ks + 3 < nks) kstep<T, NB, 3>(ks + 3, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
-  if (ks + 4 < nks) kstep<T, NB, 4>(ks + 4, acc, w0, w1, w2, xr, st, s_tile, nb_rt, r, h, brow, bp);
+  if (ks < nks) kstep<T, NB, NBR, 0>(ks, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
+  if (ks + 1 < nks) kstep<T, NB, NBR, 1>(ks + 1, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
+  if (ks + 2 < nks) kstep<T, NB, NBR, 2>(ks + 2, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
+  if (ks + 3 < nks) kstep<T, NB, NBR, 3>(ks + 3, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
+  if (ks + 4 < nks) kstep<T, NB, NBR, 4>(ks + 4, acc, w0, w1, w2, xr, st, s_tile, r, h, brow, bp);
 
   // Drain the prefetches past the end of K (they read zeros into slots that
   // are never read) so that no direct-to-LDS write is still in flight when
@@ -414,9 +397,9 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
   // Lane (r, h) holds, for column r of each 32x32 tile, rows
   // gi*8 + h*4 + [0, 4) in acc elements gi*4 .. gi*4+3.
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int nb = 0; nb < NBR; ++nb) {
     const int col = nb * 32 + r;
-    if (nb >= nb_rt || col >= mcount) continue;
+    if (col >= mcount) continue;
     if (MODE == MODE_ROUTER) {
       float *orow = static_cast<float *>(g.out) + (static_cast<int64_t>(m0) + col) * g.out_ld;
 #pragma unroll
@@ -457,6 +440,92 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
   }
 }
 
+// Live token blocks of a tile -> the specialised tile body.  bf16 dispatches
+// on every count up to NB; fp32 (a parity path, not a fast path) always runs
+// NB blocks, the empty ones reading zeros.
+template <typename T, int MODE, int NB>
+__device__ __forceinline__ void dispatch_tile(const GemmArgs &g, const TileLoc &t, int nb_rt,
+                                              char *s_w0, char *s_w1, char *s_w2,
+                                              TileBuf<NB> *s_tile) {
+  if constexpr (!std::is_same<T, bf16_t>::value || NB == 1) {
+    (void)nb_rt;
+    gemm_tile<T, MODE, NB, NB>(g, t, s_w0, s_w1, s_w2, s_tile);
+  } else {
+  switch (nb_rt) {
+#define MOEZC_TILE_CASE(n)                                                  \
+  case n:                                                                   \
+    if constexpr (n <= NB) gemm_tile<T, MODE, NB, n>(g, t, s_w0, s_w1, s_w2, s_tile); \
+    break;
+    MOEZC_TILE_CASE(1)
+    MOEZC_TILE_CASE(2)
+    MOEZC_TILE_CASE(3)
+    MOEZC_TILE_CASE(4)
+    MOEZC_TILE_CASE(5)
+    MOEZC_TILE_CASE(6)
+    MOEZC_TILE_CASE(7)
+    MOEZC_TILE_CASE(8)
+#undef MOEZC_TILE_CASE
+    default:
+      break;
+  }
+  }
+}
+
+template <typename T, int MODE, int NB>
+__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
+  constexpr int MT = NB * 32;  // tokens per chunk
+  // Three weight slots as distinct LDS objects: the compiler tracks the
+  // direct-to-LDS loads of each separately, so a read of one slot waits only
+  // for the loads into that slot.
+  __shared__ __attribute__((aligned(16))) char s_w0[kWSlotBytes];
+  __shared__ __attribute__((aligned(16))) char s_w1[kWSlotBytes];
+  __shared__ __attribute__((aligned(16))) char s_w2[kWSlotBytes];
+  __shared__ __attribute__((aligned(16))) TileBuf<NB> s_tile[2];
+
+  // ---- which tile -------------------------------------------------------
+  int ntiles;
+  if (MODE == MODE_ROUTER) {
+    ntiles = static_cast<int>((g.T + MT - 1) / MT) * g.nrb;
+  } else {
+    ntiles = g.meta[0] * g.nrb;
+  }
+  const int quota = (ntiles + 7) / 8;
+  const int loc = blockIdx.x / 8;
+  if (loc >= quota) return;
+  const int v = (blockIdx.x % 8) * quota + loc;
+  if (v >= ntiles) return;
+
+  TileLoc t;
+  t.e = 0;
+  if (MODE == MODE_ROUTER) {
+    const int nch = static_cast<int>((g.T + MT - 1) / MT);
+    t.rb = v / nch;
+    const int ch = v % nch;
+    t.m0 = ch * MT;
+    t.mcount = static_cast<int>(min<int64_t>(MT, g.T - t.m0));
+  } else {
+    // expert of chunk c: the last e with chunk_off[e] <= c (a uniform
+    // binary search over the small prefix table, read through the caches)
+    const int c = v / g.nrb;
+    const int32_t *co = g.chunk_off;
+    int lo = 0, hi = g.N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (co[mid] <= c) lo = mid;
+      else hi = mid - 1;
+    }
+    t.e = lo;
+    const int local = v - g.nrb * co[t.e];
+    const int nch = co[t.e + 1] - co[t.e];
+    t.rb = local / nch;
+    const int ch = local - t.rb * nch;
+    t.m0 = g.offs[t.e] + ch * MT;
+    t.mcount = min(MT, g.offs[t.e + 1] - t.m0);
+  }
+  const int nb_rt = (t.mcount + 31) / 32;
+  dispatch_tile<T, MODE, NB>(g, t, nb_rt, s_w0, s_w1, s_w2, s_tile);
+}
+
 // Weight rows one workgroup covers (GATE_UP: per matrix).
 static int rows_per_wg(int mode) { return mode == MODE_GATE_UP ? 128 : 256; }
 
@@ -465,7 +534,9 @@ static hipError_t launch_gemm_t(const GemmArgs &g, int nb, int64_t max_tiles, hi
   if (max_tiles <= 0) return hipSuccess;
   const int64_t grid = ((max_tiles + 7) / 8) * 8;
   const dim3 gd(static_cast<unsigned>(grid)), bd(kThreads);
-  if (nb == 4)
+  if (nb == 8)
+    hipLaunchKernelGGL((gemm_kernel<T, MODE, 8>), gd, bd, 0, s, g);
+  else if (nb == 4)
     hipLaunchKernelGGL((gemm_kernel<T, MODE, 4>), gd, bd, 0, s, g);
   else
     hipLaunchKernelGGL((gemm_kernel<T, MODE, 1>), gd, bd, 0, s, g);

@@ -143,14 +143,13 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   p.dtype = dm->dtype;
   p.nblk = static_cast<int>((T + kTokPerBlk - 1) / kTokPerBlk);
   p.pmax = T * std::min(dm->k, dm->N);
-  // Chunk height of the expert GEMMs: 128 token rows when experts receive
-  // many rows on average, else 32 (decode-shaped: weight streaming with few
-  // rows per expert wants occupancy, not tall tiles).
+  // Chunk height of the expert GEMMs (32-token blocks): 256 token rows when
+  // experts receive many rows on average, so that an expert's weights stream
+  // once (a second chunk streams them again); 128 in between; 32 when they
+  // receive few (decode-shaped: weight streaming with few rows per expert
+  // wants occupancy, not tall tiles).
   const int64_t avg_rows = dm->N > 0 ? p.pmax / dm->N : 0;
-#ifndef MOEZC_NB_BIG
-#define MOEZC_NB_BIG 4
-#endif
-  p.nbmax = avg_rows >= 48 ? MOEZC_NB_BIG : 1;
+  p.nbmax = avg_rows >= 96 ? 8 : (avg_rows >= 24 ? 4 : 1);
   p.x = x;
   p.w_router = w_router;
   p.w_gate = w_gate;
