@@ -57,6 +57,43 @@ def algorithmic(cfg, counts):
             "gate_up": gate_up, "down": down, "router": router}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+# HBM traffic of the dominant kernel, measured by rocprofv3 --pmc FETCH_SIZE
+# and WRITE_SIZE in their own runs and kept in a committed summary together
+# with the hash of the kernel source it was measured on; a summary taken on
+# another version of the kernel is not reported.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_prod_hbm_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "zero_computation_expert_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic(workload):
+    import hashlib
+
+    if workload != "prod" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(cfg, dinp, ntok):
     """The oracle, as it is, on the first `ntok` tokens of the same workload."""
     import numpy as np
@@ -77,7 +114,8 @@ def cpu_baseline(cfg, dinp, ntok):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {ntok} of {cfg.T} tokens of the same workload (whole forward: "
-                      f"router, top-k, experts, combine); {dt:.1f}s of oracle time, "
+                      f"router, top-k, experts, combine); {dt:.1f}s of oracle time on "
+                      f"{threads} OpenMP threads of a {cpu_model()}, "
                       f"{prep:.1f}s input prep excluded"}
 
 
@@ -159,7 +197,7 @@ def main():
     gu_gbs = alg["gate_up"]["bytes"] / gu_s / 1e9
     roofline = {"bound": "hbm", "kernel": "gemm_kernel<bf16,GATE_UP> (gate/up GEMM + SwiGLU)",
                 "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
                 "algorithmic_bytes_per_launch": alg["gate_up"]["bytes"],
                 "avg_launch_ms": round(stage_avg["gate_up"], 4)}
     kernels = {}
@@ -195,7 +233,7 @@ def main():
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        ntok = args.cpu_tokens or {"prod": 128, "skewed": 128, "decode": 128, "small": 512,
+        ntok = args.cpu_tokens or {"prod": 1536, "skewed": 1536, "decode": 128, "small": 4096,
                                    "tiny": 64}[cfg.name]
         res["cpu_baseline"] = cpu_baseline(cfg, inp, min(ntok, cfg.T))
     print(json.dumps(res), flush=True)
