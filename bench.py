@@ -232,6 +232,21 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
         "kernels": kernels,
     }
+    # bias controller (the step that consumes counts between forward calls),
+    # timed on its own over 200 calls on the same stream
+    target = torch.full((cfg.E,), float(cfg.T * cfg.k) / cfg.E, dtype=torch.float32, device=dev)
+    bias_c = inp["bias"].clone()
+    state = torch.zeros(2 * cfg.E, dtype=torch.float32, device=dev)
+    moe.bias_update(counts, target, bias_c, cfg.T, 1e-3, 1.0, 0.5, 0.0, state, 0)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(200):
+        moe.bias_update(counts, target, bias_c, cfg.T, 1e-3, 1.0, 0.5, 0.0, state, 0)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    bu_us = ev0.elapsed_time(ev1) / 200 * 1e3
+    res["bias_update"] = {"us_per_call": round(bu_us, 2), "experts": cfg.E,
+                          "bytes_per_call": cfg.E * 32, "bound": "launch latency"}
     if not args.no_cpu_baseline:
         ntok = args.cpu_tokens or {"prod": 1536, "skewed": 1536, "decode": 128, "small": 4096,
                                    "tiny": 64}[cfg.name]

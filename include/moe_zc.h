@@ -101,6 +101,39 @@ int moe_zc_forward(const moe_zc_dims *dims, const void *x, const void *W_router,
 const char *moe_zc_status_string(int status);
 
 /* ------------------------------------------------------------------------
+ * Bias controller: the consumer of `counts`, run between forward calls.
+ *
+ * LongCat-Flash technical-report summary page, section 2 "architecture",
+ * computation-budget control (also section 1, main contributions): an
+ * expert-specific bias, adjusted by a PID controller, keeps the average
+ * share of FFN vs zero-computation experts near its target.  The pages give
+ * no formula or gains.  This library's reading, per expert e, in fp32 in
+ * this order with no fused operations (bit-reproducible):
+ *   err = (target[e] - counts[e]) / T            per-token load error
+ *   mode 0 (incremental PID):
+ *     u = ki*err + kp*(err - e1) + kd*((err - e1) - (e1 - e2))
+ *     bias[e] += lr * u
+ *   mode 1 (sign update, aux-loss-free style):
+ *     bias[e] += lr * sign(err)                   (sign(0) = 0)
+ * An under-selected expert (err > 0) gets a larger bias, so it is selected
+ * more.  The caller owns the schedule (pass the decayed lr each call) and
+ * the targets (e.g. share * T * k / N for each FFN expert and
+ * (1 - share) * T * k / Z for each zero expert; they need not sum to T*k).
+ *   counts  [E]    int32, as written by moe_zc_forward for a batch of T tokens
+ *   target  [E]    fp32 desired selections per expert for that batch
+ *   bias    [E]    fp32, updated in place
+ *   state   [2*E]  fp32 (e1, e2) per expert, updated in place (e1 <- err,
+ *                  e2 <- old e1); zero it before the first call.  Nullable:
+ *                  then e1 = e2 = err, i.e. a pure integral step.
+ * Device pointers, 4-byte aligned, owned by the caller; asynchronous on
+ * `stream`.  MOE_ZC_EINVAL if E < 1, T < 1, a required pointer is NULL,
+ * mode is not 0 or 1, or a gain or lr is not finite; MOE_ZC_EALIGN for a
+ * misaligned pointer; nothing is enqueued on error. */
+int moe_zc_bias_update(int32_t E, int64_t T, const int32_t *counts, const float *target,
+                       float *bias, float *state, float lr, float ki, float kp, float kd,
+                       int32_t mode, void *stream);
+
+/* ------------------------------------------------------------------------
  * Per-stage timing (measurement aid).  A timer owns HIP events for up to
  * `max_calls` forward calls; moe_zc_forward_timed records an event before
  * the first and after every stage on `stream`.  moe_zc_timer_read waits for

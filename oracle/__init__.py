@@ -60,6 +60,8 @@ def _load():
                                                      vp, vp, vp, vp]
         lib.oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, vp, vp]
+        f32 = ctypes.c_float
+        lib.oracle_bias_update.argtypes = [i32, i64, vp, vp, vp, vp, f32, f32, f32, f32, i32]
         _lib = lib
     return _lib
 
@@ -173,3 +175,19 @@ def forward(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, k: int, dt:
                            _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(cnt), _ptr(idx),
                            _ptr(gate), _ptr(margin))
     return {"out": out, "counts": cnt, "idx": idx, "gate": gate, "margin": margin}
+
+
+def bias_update(counts, target, bias, T: int, lr: float, ki: float = 1.0, kp: float = 0.0,
+                kd: float = 0.0, state=None, mode: int = 0):
+    """Bias controller step (see oracle.c).  Returns (new bias, new state or
+    None); the inputs are not modified."""
+    counts = _c(counts, np.int32)
+    target = _c(target, np.float32)
+    b = np.array(bias, dtype=np.float32, copy=True)
+    st = None if state is None else np.array(state, dtype=np.float32, copy=True)
+    E = b.shape[0]
+    assert counts.shape == (E,) and target.shape == (E,)
+    assert st is None or st.shape == (2 * E,)
+    _load().oracle_bias_update(E, T, _ptr(counts), _ptr(target), _ptr(b), _ptr(st),
+                               float(lr), float(ki), float(kp), float(kd), int(mode))
+    return b, st

@@ -220,3 +220,46 @@ void oracle_forward(int64_t T, int d, int I, int N, int Z, int k, int dt, const 
   oracle_combine_given_routing(T, d, I, N, k, x, dt, idx, gate, w_gate, w_up, w_down, out);
   free(logits);
 }
+
+/* Bias controller (the step after the forward that consumes `counts`).
+ * [LCF-arch] computation-budget control, and [LCF] section 1 "main
+ * contributions": an expert-specific bias, adjusted by a PID controller,
+ * keeps the average share of FFN vs zero experts near its target.  [KOL]:
+ * the balancing is aux-loss-free, a bias update with a decaying step.  The
+ * pages give no formula or gains; this is the plain incremental PID on the
+ * per-token load error of each expert:
+ *   e   = (target[e] - counts[e]) / T                   (selections per token)
+ *   u   = ki*e + kp*(e - e1) + kd*((e - e1) - (e1 - e2))  (e1, e2: previous two e)
+ *   bias[e] += lr * u                                   (mode 0)
+ *   bias[e] += lr * sign(e)                             (mode 1, sign update)
+ * The caller supplies lr (its decay schedule) and the per-expert target.  An
+ * under-selected expert (e > 0) gets a larger bias, hence more selections.
+ * state[2*E] = (e1, e2) per expert, updated in place; NULL means "no history"
+ * (e1 = e2 = e).  All fp32, in this order, with no contraction. */
+void oracle_bias_update(int E, int64_t T, const int32_t *counts, const float *target, float *bias,
+                        float *state, float lr, float ki, float kp, float kd, int mode) {
+  const float tf = (float)T;
+  for (int e = 0; e < E; ++e) {
+    const float err = (target[e] - (float)counts[e]) / tf;
+    float step;
+    if (mode == 1) {
+      const float s = err > 0.0f ? 1.0f : (err < 0.0f ? -1.0f : 0.0f);
+      step = lr * s;
+    } else {
+      const float e1 = state ? state[2 * e] : err;
+      const float e2 = state ? state[2 * e + 1] : err;
+      const float a = err - e1;
+      const float b = e1 - e2;
+      const float dd = a - b;
+      float u = ki * err;
+      u = u + kp * a;
+      u = u + kd * dd;
+      step = lr * u;
+    }
+    bias[e] = bias[e] + step;
+    if (state) {
+      state[2 * e + 1] = state[2 * e];
+      state[2 * e] = err;
+    }
+  }
+}

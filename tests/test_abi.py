@@ -133,3 +133,28 @@ def test_product_package_has_no_cpu_path():
     assert "import numpy" not in src
     for f in os.listdir(os.path.join(ROOT, "zero_computation_expert_amd", "csrc")):
         assert "oracle" not in open(os.path.join(ROOT, "zero_computation_expert_amd", "csrc", f)).read()
+
+
+def bias_call(E=16, T=64, counts=A, target=2 * A, bias=3 * A, state=None, lr=0.1, ki=1.0,
+              kp=0.0, kd=0.0, mode=0):
+    st = moe.lib().moe_zc_bias_update(E, T, counts, target, bias, state, lr, ki, kp, kd, mode,
+                                      None)
+    assert st != 0, "a test call passed validation: it would have launched work"
+    return st
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(E=0), EINVAL),
+    (dict(E=-3), EINVAL),
+    (dict(T=0), EINVAL),
+    (dict(counts=None), EINVAL),
+    (dict(target=None), EINVAL),
+    (dict(bias=None), EINVAL),
+    (dict(mode=2), EINVAL),
+    (dict(lr=float("nan")), EINVAL),
+    (dict(kp=float("inf")), EINVAL),
+    (dict(bias=3 * A + 2), EALIGN),
+    (dict(state=A + 1), EALIGN),
+])
+def test_bias_update_rejects(kw, expect):
+    assert bias_call(**kw) == expect

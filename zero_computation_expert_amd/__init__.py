@@ -21,7 +21,7 @@ STATUS = {0: "MOE_ZC_OK", -1: "MOE_ZC_EINVAL", -2: "MOE_ZC_EDTYPE", -3: "MOE_ZC_
 STAGES = ("router", "topk", "scan", "permute", "gate_up", "down", "combine")
 EXPORTS = ("moe_zc_workspace_bytes", "moe_zc_forward", "moe_zc_status_string",
            "moe_zc_timer_create", "moe_zc_forward_timed", "moe_zc_timer_read",
-           "moe_zc_timer_reset", "moe_zc_timer_destroy")
+           "moe_zc_timer_reset", "moe_zc_timer_destroy", "moe_zc_bias_update")
 
 
 class MoeZcError(RuntimeError):
@@ -66,6 +66,10 @@ def lib():
         L.moe_zc_timer_reset.argtypes = [vp]
         L.moe_zc_timer_destroy.restype = None
         L.moe_zc_timer_destroy.argtypes = [vp]
+        f32 = ctypes.c_float
+        L.moe_zc_bias_update.restype = ctypes.c_int
+        L.moe_zc_bias_update.argtypes = [ctypes.c_int32, ctypes.c_int64, vp, vp, vp, vp, f32, f32,
+                                         f32, f32, ctypes.c_int32, vp]
         _lib = L
     return _lib
 
@@ -175,3 +179,18 @@ def forward(x, W_router, bias, W_gate, W_up, W_down, N: int, Z: int, k: int, *,
         st = lib().moe_zc_forward_timed(*args, timer.handle)
     _check(st)
     return out, counts, topk_idx, topk_gate
+
+
+def bias_update(counts, target, bias, T: int, lr: float, ki: float = 1.0, kp: float = 0.0,
+                kd: float = 0.0, state=None, mode: int = 0, stream=None):
+    """Runs moe_zc_bias_update in place on torch device tensors: counts int32
+    [E], target and bias float32 [E], state float32 [2E] or None."""
+    import torch
+
+    E = bias.numel()
+    if stream is None:
+        stream = torch.cuda.current_stream(bias.device).cuda_stream
+    _check(lib().moe_zc_bias_update(int(E), int(T), _ptr(counts), _ptr(target), _ptr(bias),
+                                    _ptr(state), float(lr), float(ki), float(kp), float(kd),
+                                    int(mode), stream))
+    return bias, state
