@@ -10,7 +10,7 @@
 namespace moezc {
 
 constexpr int kWave = 64;
-constexpr int kTokPerBlk = 64;  // tokens per top-k / permutation block
+constexpr int kTokPerBlk = 16;  // tokens per top-k / permutation block (one wave each in top-k)
 constexpr int kMaxE = 2048;     // experts the top-k kernel holds in registers
 constexpr int kMaxK = 64;       // slots per token (one lane per slot)
 
@@ -58,15 +58,35 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// One step of a DPP maximum over (hi, lo) 64-bit keys: each lane compares
+// its key with the one the DPP control selects (lanes without a source, and
+// lanes outside ROW_MASK, see zero or themselves; 0 is the smallest key).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_max_step(uint32_t &hi, uint32_t &lo) {
+  const uint32_t h2 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(hi), static_cast<int>(hi), CTRL, ROW_MASK, 0xF, true));
+  const uint32_t l2 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(lo), static_cast<int>(lo), CTRL, ROW_MASK, 0xF, true));
+  const bool take = h2 > hi || (h2 == hi && l2 > lo);
+  hi = take ? h2 : hi;
+  lo = take ? l2 : lo;
+}
+
+// Maximum of a 64-bit key over the (fully active) wave, returned to every
+// lane: prefix maxima within each row of 16 lanes (row_shr 1, 2, 4, 8), then
+// the gfx9 row broadcasts (lane 15 of each row into the next row, lane 31
+// into rows 2 and 3) leave the wave maximum in lane 63.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, kWave);
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, kWave);
-    uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
+  uint32_t hi = static_cast<uint32_t>(v >> 32), lo = static_cast<uint32_t>(v);
+  dpp_max_step<0x111, 0xF>(hi, lo);  // row_shr:1
+  dpp_max_step<0x112, 0xF>(hi, lo);  // row_shr:2
+  dpp_max_step<0x114, 0xF>(hi, lo);  // row_shr:4
+  dpp_max_step<0x118, 0xF>(hi, lo);  // row_shr:8
+  dpp_max_step<0x142, 0xA>(hi, lo);  // row_bcast:15
+  dpp_max_step<0x143, 0xC>(hi, lo);  // row_bcast:31
+  hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 63));
+  lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 63));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // ---- launchers (host side), one per stage ------------------------------

@@ -23,10 +23,10 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
 // Selection key = (ordered score << 32) | (0xffffffff - e): the wave maximum
 // is the highest score and, among equal scores, the lowest index.  Key 0
 // marks a taken or absent expert (every real key is > 0).
-// The block (4 waves) covers kTokPerBlk consecutive tokens and writes its
-// per-expert selection histogram to blockhist[blockIdx.x].
+// The block (kTokPerBlk waves) covers kTokPerBlk consecutive tokens and
+// writes its per-expert selection histogram to blockhist[blockIdx.x].
 template <int VPL>
-__global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits,
+__global__ void __launch_bounds__(kTokPerBlk * kWave) topk_kernel(const float *__restrict__ logits,
                                                    const float *__restrict__ bias, int64_t T,
                                                    int E, int k, int32_t *__restrict__ idx_out,
                                                    float *__restrict__ gate_out,
@@ -43,9 +43,8 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ log
   const int wave = threadIdx.x / kWave;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokPerBlk;
 
-  for (int tt = wave; tt < kTokPerBlk; tt += 4) {
-    const int64_t t = t0 + tt;
-    if (t >= T) break;
+  const int64_t t = t0 + wave;
+  if (t < T) {
     const float *lrow = logits + t * E;
     float l[VPL];
 #pragma unroll
@@ -237,7 +236,7 @@ __global__ void zero_int_kernel(int32_t *p, int n) {
 }
 
 hipError_t launch_topk(const Plan &p, hipStream_t s) {
-  dim3 grid(p.nblk), block(256);
+  dim3 grid(p.nblk), block(kTokPerBlk * kWave);
   int vpl = (p.E + kWave - 1) / kWave;
   if (vpl <= 4)
     hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p.logits, p.bias, p.T, p.E, p.k, p.idx,
