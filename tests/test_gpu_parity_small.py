@@ -82,6 +82,14 @@ def test_parity_full(cfg):
     full_check(cfg, synth.host_inputs(cfg), poison=True)
 
 
+def test_maximum_expert_count_and_k():
+    """The library's limits: E = 2048 experts (1024 FFN + 1024 zero), k = 64
+    slots per token; the widest top-k variant and 8 router row blocks."""
+    cfg = synth.Config("maxE", T=40, d=64, I=16, N=1024, Z=1024, k=64, dtype="bf16", seed=13,
+                       bias_lo=-1e-4, bias_hi=1e-4)
+    full_check(cfg, synth.host_inputs(cfg), poison=True)
+
+
 def test_deterministic_bitwise():
     cfg = RAGGED[1]
     inp = synth.host_inputs(cfg)

@@ -70,6 +70,9 @@ struct GemmArgs {
   int out_ld;                // elements per output row
   int nrb;                   // row blocks per chunk
   int N;                     // FFN experts (GATE_UP, DOWN)
+  int split;                 // ROUTER: K slices (1 = no split)
+  int kslice;                // ROUTER: K elements per slice
+  int64_t part_stride;       // ROUTER: elements between slices' partial logits
 };
 
 template <typename T>
@@ -281,9 +284,12 @@ __device__ __forceinline__ void kstep(int ks, floatx16 (&acc)[2][NBR], char *w0,
   tile_barrier();
 }
 
-// Where a tile sits: expert e, weight row block rb, token rows [m0, m0 + mcount).
+// Where a tile sits: expert e, weight row block rb, token rows
+// [m0, m0 + mcount), and the K range [k0, k0 + klen) it reduces over (all of
+// K except for a split router GEMM, whose slice s writes partial logits).
 struct TileLoc {
   int e, rb, m0, mcount;
+  int k0, klen, s;
 };
 
 // The whole K loop and epilogue of one tile with NBR live 32-token blocks
@@ -294,15 +300,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t, c
   constexpr int KC = 128 / sizeof(T);  // K elements per step (128 bytes per row)
   constexpr uint32_t ES = sizeof(T);
   const int e = t.e, rb = t.rb, m0 = t.m0, mcount = t.mcount;
+  const uint32_t kbyte0 = static_cast<uint32_t>(t.k0) * ES;  // first byte of the K range in a row
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 31;
   const int h = lane >> 5;
-  const int K = g.K;
+  const int K = g.K;  // row length (elements); this tile reduces over t.klen of them
 
   TileState<NBR> st;
-  st.K = K;
+  st.K = t.klen;
   // ---- the 64 weight rows of this wave (MFMA A operand) -------------------
   const uint32_t wbytes = static_cast<uint32_t>(g.nrows) * static_cast<uint32_t>(K) * ES;
   int rowbase[2];  // first weight row of each 32-row block
@@ -325,7 +332,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t, c
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        st.wrow[a][j] = static_cast<uint32_t>(min(rowbase[a] + j * 8 + lr, g.nrows - 1)) * K * ES;
+        st.wrow[a][j] =
+            static_cast<uint32_t>(min(rowbase[a] + j * 8 + lr, g.nrows - 1)) * K * ES + kbyte0;
   }
 
   // ---- token rows this thread stages into LDS (B operand) ----------------
@@ -343,10 +351,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t, c
     const int tr = brow + 32 * i;
     uint32_t row = 0;
     if (tr < mcount) row = MODE == MODE_GATE_UP ? static_cast<uint32_t>(g.tok[m0 + tr]) : tr;
-    st.vob[i] = tr < mcount ? row * K * ES + bp * 16 : kOOB;
+    st.vob[i] = tr < mcount ? row * K * ES + kbyte0 + bp * 16 : kOOB;
   }
 
-  const int nks = (K + KC - 1) / KC;
+  const int nks = (t.klen + KC - 1) / KC;
   char *const w0 = s_w0 + wave * kWaveRowBytes;
   char *const w1 = s_w1 + wave * kWaveRowBytes;
   char *const w2 = s_w2 + wave * kWaveRowBytes;
@@ -401,7 +409,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t, c
     const int col = nb * 32 + r;
     if (col >= mcount) continue;
     if (MODE == MODE_ROUTER) {
-      float *orow = static_cast<float *>(g.out) + (static_cast<int64_t>(m0) + col) * g.out_ld;
+      float *orow = static_cast<float *>(g.out) + t.s * g.part_stride +
+                    (static_cast<int64_t>(m0) + col) * g.out_ld;
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -485,7 +494,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
   // ---- which tile -------------------------------------------------------
   int ntiles;
   if (MODE == MODE_ROUTER) {
-    ntiles = static_cast<int>((g.T + MT - 1) / MT) * g.nrb;
+    ntiles = static_cast<int>((g.T + MT - 1) / MT) * g.nrb * g.split;
   } else {
     ntiles = g.meta[0] * g.nrb;
   }
@@ -497,12 +506,20 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
 
   TileLoc t;
   t.e = 0;
+  t.k0 = 0;
+  t.klen = g.K;
+  t.s = 0;
   if (MODE == MODE_ROUTER) {
+    // K slice outermost, then row block, then token chunk
     const int nch = static_cast<int>((g.T + MT - 1) / MT);
-    t.rb = v / nch;
-    const int ch = v % nch;
+    t.s = v / (g.nrb * nch);
+    const int rem = v - t.s * g.nrb * nch;
+    t.rb = rem / nch;
+    const int ch = rem % nch;
     t.m0 = ch * MT;
     t.mcount = static_cast<int>(min<int64_t>(MT, g.T - t.m0));
+    t.k0 = t.s * g.kslice;
+    t.klen = min(g.kslice, g.K - t.k0);
   } else {
     // expert of chunk c: the last e with chunk_off[e] <= c (a uniform
     // binary search over the small prefix table, read through the caches)
@@ -566,8 +583,11 @@ hipError_t launch_router_gemm(const Plan &p, hipStream_t s) {
   g.nrows = p.E;
   g.out_ld = p.E;
   g.nrb = (p.E + rows_per_wg(MODE_ROUTER) - 1) / rows_per_wg(MODE_ROUTER);
-  const int nb = 4;
-  const int64_t tiles = ((p.T + 32 * nb - 1) / (32 * nb)) * g.nrb;
+  g.split = p.rs.split;
+  g.kslice = p.rs.kslice;
+  g.part_stride = p.T * p.E;
+  const int nb = p.rs.nb;
+  const int64_t tiles = ((p.T + 32 * nb - 1) / (32 * nb)) * g.nrb * g.split;
   return launch_gemm<MODE_ROUTER>(p, g, nb, tiles, s);
 }
 
@@ -588,6 +608,7 @@ hipError_t launch_gate_up(const Plan &p, hipStream_t s) {
   g.out_ld = p.I;
   g.nrb = (p.I + rows_per_wg(MODE_GATE_UP) - 1) / rows_per_wg(MODE_GATE_UP);
   g.N = p.N;
+  g.split = 1;
   return launch_gemm<MODE_GATE_UP>(p, g, p.nbmax, max_chunks(p) * g.nrb, s);
 }
 
@@ -605,6 +626,7 @@ hipError_t launch_down(const Plan &p, hipStream_t s) {
   g.out_ld = p.d;
   g.nrb = (p.d + rows_per_wg(MODE_DOWN) - 1) / rows_per_wg(MODE_DOWN);
   g.N = p.N;
+  g.split = 1;
   return launch_gemm<MODE_DOWN>(p, g, p.nbmax, max_chunks(p) * g.nrb, s);
 }
 

@@ -57,7 +57,8 @@ static size_t layout(const moe_zc_dims *dm, char *base, Plan *p) {
     off = align_up(off + bytes);
     return ptr;
   };
-  char *logits = take(static_cast<size_t>(T) * E * 4);
+  const RouterSplit rs = router_split(T, dm->d, E, dm->dtype);
+  char *logits = take(static_cast<size_t>(rs.split) * T * E * 4);
   char *blockhist = take(static_cast<size_t>(nblk) * E * 4);
   char *offs = take(static_cast<size_t>(dm->N + 1) * 4);
   char *chunk_off = take(static_cast<size_t>(dm->N + 1) * 4);
@@ -150,6 +151,7 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   // wants occupancy, not tall tiles).
   const int64_t avg_rows = dm->N > 0 ? p.pmax / dm->N : 0;
   p.nbmax = avg_rows >= 96 ? 8 : (avg_rows >= 24 ? 4 : 1);
+  p.rs = router_split(T, p.d, p.E, p.dtype);
   p.x = x;
   p.w_router = w_router;
   p.w_gate = w_gate;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "moe_zc.h"
 
 namespace moezc {
@@ -89,6 +91,32 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Router GEMM partition (host side, a pure function of the sizes so that the
+// workspace query and the launch agree).  Token chunks of 32*nb rows, 256
+// expert rows per workgroup; when that leaves the 256 CUs short of work
+// (decode-sized batches, few experts), the K range is split into `split`
+// slices of `kslice` elements (whole 128-byte steps, at least two per slice)
+// whose fp32 partial logits are summed by the top-k kernel in slice order
+// (at most kMaxSplit slices, so that sum stays short).
+constexpr int kMaxSplit = 16;
+struct RouterSplit {
+  int nb, split, kslice;
+};
+inline RouterSplit router_split(int64_t T, int d, int E, int dtype) {
+  const int kc = dtype == MOE_ZC_BF16 ? 64 : 32;  // K elements per 128-byte step
+  RouterSplit r;
+  r.nb = T >= 128 ? 4 : 1;
+  const int64_t chunks = (T + 32 * r.nb - 1) / (32 * r.nb);
+  const int64_t tiles = std::max<int64_t>(1, chunks * ((E + 255) / 256));
+  const int nks = (d + kc - 1) / kc;
+  int64_t want = std::min<int64_t>(std::min<int64_t>(256 / tiles, nks / 2), kMaxSplit);
+  want = std::max<int64_t>(want, 1);
+  const int steps = static_cast<int>((nks + want - 1) / want);
+  r.kslice = steps * kc;
+  r.split = (d + r.kslice - 1) / r.kslice;
+  return r;
+}
+
 // ---- launchers (host side), one per stage ------------------------------
 struct Plan;  // defined in moe_zc.cpp
 
@@ -110,6 +138,7 @@ struct Plan {
   int nblk;   // ceil(T / kTokPerBlk)
   int64_t pmax;  // T * min(k, N): upper bound of (token, FFN expert) pairs
   int nbmax;  // 32-token column blocks per GEMM chunk (1, 4 or 8)
+  RouterSplit rs;  // router GEMM partition
   // caller tensors
   const void *x, *w_router, *w_gate, *w_up, *w_down;
   const float *bias;
@@ -118,7 +147,7 @@ struct Plan {
   int32_t *idx;   // caller's or workspace
   float *gate;    // caller's or workspace
   // workspace
-  float *logits;        // [T, E]
+  float *logits;        // [rs.split, T, E] partial router logits (one slice of K each)
   int32_t *blockhist;   // [nblk, E]: per-block counts, then exclusive prefixes
   int32_t *offs;        // [N + 1] row offset of each FFN expert in permuted order
   int32_t *chunk_off;   // [N + 1] exclusive prefix of GEMM chunks per expert

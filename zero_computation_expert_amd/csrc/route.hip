@@ -27,6 +27,7 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
 // writes its per-expert selection histogram to blockhist[blockIdx.x].
 template <int VPL>
 __global__ void __launch_bounds__(kTokPerBlk * kWave) topk_kernel(const float *__restrict__ logits,
+                                                   int split, int64_t part_stride,
                                                    const float *__restrict__ bias, int64_t T,
                                                    int E, int k, int32_t *__restrict__ idx_out,
                                                    float *__restrict__ gate_out,
@@ -51,6 +52,32 @@ __global__ void __launch_bounds__(kTokPerBlk * kWave) topk_kernel(const float *_
     for (int s = 0; s < VPL; ++s) {
       int e = s * kWave + lane;
       l[s] = e < E ? lrow[e] : -INFINITY;
+    }
+    // A split router GEMM leaves one partial per K slice: add them in slice
+    // order, loading U slices at a time so their loads overlap (U = 1 for the
+    // widest expert counts, whose registers are already full).
+    constexpr int U = VPL <= 16 ? 4 : 1;
+    int sl = 1;
+    for (; sl + U <= split; sl += U) {
+      float a[U][VPL];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int s = 0; s < VPL; ++s) {
+          int e = s * kWave + lane;
+          a[u][s] = e < E ? lrow[(sl + u) * part_stride + e] : 0.0f;
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int s = 0; s < VPL; ++s) l[s] += a[u][s];
+    }
+    for (; sl < split; ++sl) {
+#pragma unroll
+      for (int s = 0; s < VPL; ++s) {
+        int e = s * kWave + lane;
+        if (e < E) l[s] += lrow[sl * part_stride + e];
+      }
     }
     float m = l[0];
 #pragma unroll
@@ -239,13 +266,13 @@ hipError_t launch_topk(const Plan &p, hipStream_t s) {
   dim3 grid(p.nblk), block(kTokPerBlk * kWave);
   int vpl = (p.E + kWave - 1) / kWave;
   if (vpl <= 4)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p.logits, p.bias, p.T, p.E, p.k, p.idx,
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k, p.idx,
                        p.gate, p.blockhist);
   else if (vpl <= 16)
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p.logits, p.bias, p.T, p.E, p.k,
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k,
                        p.idx, p.gate, p.blockhist);
   else
-    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p.logits, p.bias, p.T, p.E, p.k,
+    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k,
                        p.idx, p.gate, p.blockhist);
   return hipGetLastError();
 }
