@@ -62,6 +62,17 @@ def _load():
                                        vp, vp, vp, vp, vp]
         f32 = ctypes.c_float
         lib.oracle_bias_update.argtypes = [i32, i64, vp, vp, vp, vp, f32, f32, f32, f32, i32]
+        lib.oracle_e4m3_from_f32.restype = ctypes.c_uint8
+        lib.oracle_e4m3_from_f32.argtypes = [f32]
+        lib.oracle_e4m3_to_f32.restype = f32
+        lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        lib.oracle_quantize_fp8.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp]
+        lib.oracle_token_output_fp8.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
+                                                vp, vp, vp, vp]
+        lib.oracle_combine_given_routing_fp8.argtypes = [i64, i32, i32, i32, i32, vp, i32, vp, vp,
+                                                         vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_forward_fp8.argtypes = [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -191,3 +202,93 @@ def bias_update(counts, target, bias, T: int, lr: float, ki: float = 1.0, kp: fl
     _load().oracle_bias_update(E, T, _ptr(counts), _ptr(target), _ptr(b), _ptr(st),
                                float(lr), float(ki), float(kp), float(kd), int(mode))
     return b, st
+
+
+# ---------------------------------------------------------------------------
+# Block-scaled FP8 experts (see oracle.c for the readings)
+# ---------------------------------------------------------------------------
+
+def e4m3_from_f32(v: float) -> int:
+    return int(_load().oracle_e4m3_from_f32(float(v)))
+
+
+def e4m3_to_f32(q: int) -> float:
+    return float(_load().oracle_e4m3_to_f32(int(q)))
+
+
+def quantize_fp8(src, dt: str, block_rows: int):
+    """src [nmat, rows, K] (or [rows, K]) in storage dtype -> (q uint8 same
+    shape, scales float32 [nmat, rows/block_rows, K/128])."""
+    a = _storage(src, dt)
+    shape = a.shape
+    if a.ndim == 2:
+        a = a[None]
+    nmat, rows, K = a.shape
+    assert rows % block_rows == 0 and K % 128 == 0
+    q = np.empty(a.shape, dtype=np.uint8)
+    sc = np.empty((nmat, rows // block_rows, K // 128), dtype=np.float32)
+    _load().oracle_quantize_fp8(_ptr(a), _DT[dt], nmat, rows, K, block_rows, _ptr(q), _ptr(sc))
+    if len(shape) == 2:
+        return q[0], sc[0]
+    return q, sc
+
+
+def token_output_fp8(x_row, dt: str, N: int, idx_row, gate_row, experts: dict) -> np.ndarray:
+    """One token with FP8 experts; ``experts[e] = (qWg, sWg, qWu, sWu, qWd, sWd)``."""
+    x_row = _storage(x_row, dt)
+    d = x_row.shape[0]
+    idx_row = _c(idx_row, np.int32)
+    gate_row = _c(gate_row, np.float32)
+    k = idx_row.shape[0]
+    arrs = [(ctypes.c_void_p * k)() for _ in range(6)]
+    keep = []
+    I = 128
+    for j in range(k):
+        e = int(idx_row[j])
+        if e < N:
+            ex = [_c(a, np.uint8 if i % 2 == 0 else np.float32) for i, a in enumerate(experts[e])]
+            keep += ex
+            I = ex[0].shape[0]
+            for i in range(6):
+                arrs[i][j] = ex[i].ctypes.data
+    out = np.empty(d, dtype=np.float32)
+    _load().oracle_token_output_fp8(d, I, N, k, _ptr(x_row), _DT[dt], _ptr(idx_row),
+                                    _ptr(gate_row), *arrs, _ptr(out))
+    return out
+
+
+def combine_given_routing_fp8(x, dt, N, idx, gate, qwg, swg, qwu, swu, qwd, swd) -> np.ndarray:
+    x = _storage(x, dt)
+    T, d = x.shape
+    idx = _c(idx, np.int32)
+    gate = _c(gate, np.float32)
+    k = idx.shape[1]
+    qwg, qwu, qwd = (_c(a, np.uint8) for a in (qwg, qwu, qwd))
+    swg, swu, swd = (_c(a, np.float32) for a in (swg, swu, swd))
+    I = qwg.shape[1]
+    out = np.empty((T, d), dtype=np.float32)
+    _load().oracle_combine_given_routing_fp8(T, d, I, N, k, _ptr(x), _DT[dt], _ptr(idx),
+                                             _ptr(gate), _ptr(qwg), _ptr(swg), _ptr(qwu),
+                                             _ptr(swu), _ptr(qwd), _ptr(swd), _ptr(out))
+    return out
+
+
+def forward_fp8(x, w_router, bias, qwg, swg, qwu, swu, qwd, swd, N: int, Z: int, k: int, dt: str):
+    """Whole FP8-expert forward. Returns dict(out, counts, idx, gate, margin)."""
+    x = _storage(x, dt)
+    w_router = _storage(w_router, dt)
+    bias = _c(bias, np.float32)
+    T, d = x.shape
+    E = N + Z
+    qwg, qwu, qwd = (_c(a, np.uint8) for a in (qwg, qwu, qwd))
+    swg, swu, swd = (_c(a, np.float32) for a in (swg, swu, swd))
+    I = qwg.shape[1]
+    out = np.empty((T, d), dtype=np.float32)
+    cnt = np.empty(E, dtype=np.int32)
+    idx = np.empty((T, k), dtype=np.int32)
+    gate = np.empty((T, k), dtype=np.float32)
+    margin = np.empty(T, dtype=np.float32)
+    _load().oracle_forward_fp8(T, d, I, N, Z, k, _DT[dt], _ptr(x), _ptr(w_router), _ptr(bias),
+                               _ptr(qwg), _ptr(swg), _ptr(qwu), _ptr(swu), _ptr(qwd), _ptr(swd),
+                               _ptr(out), _ptr(cnt), _ptr(idx), _ptr(gate), _ptr(margin))
+    return {"out": out, "counts": cnt, "idx": idx, "gate": gate, "margin": margin}

@@ -263,3 +263,210 @@ void oracle_bias_update(int E, int64_t T, const int32_t *counts, const float *ta
     }
   }
 }
+
+/* ------------------------------------------------------------------------
+ * Block-scaled FP8 experts.
+ * [LCF] section 6 "inference and deployment", custom kernels, quantization
+ * item: fine-grained block quantization as in DeepSeek-V3, activations per
+ * [1,128] block and weights per [128,128] block.  Readings (the pages name
+ * neither the format nor the scale rule):
+ *   - FP8 = OCP E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits,
+ *     subnormals, largest finite 448, no infinities;
+ *   - conversion rounds to nearest, ties to even, and saturates at +-448;
+ *   - a block's scale is amax / 448 (1 for an all-zero block), q = E4M3(v /
+ *     scale), so the block's largest magnitude maps to 448;
+ *   - a GEMM adds, per 128-wide K block, (scale_a * scale_b) times the fp32
+ *     sum of the products of the quantized values;
+ *   - the router stays in the inputs' dtype; x is quantized per [1,128]
+ *     before the gate/up projections, the SwiGLU activations per [1,128]
+ *     before the down projection; a zero expert returns the unquantized x.
+ * ------------------------------------------------------------------------ */
+
+/* E4M3 byte of a finite fp32 value (round to nearest even, saturate). */
+uint8_t oracle_e4m3_from_f32(float v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const float a = fabsf(v);
+  if (a > 448.0f) return sign | 0x7E;
+  if (a < 0.015625f) {                     /* below 2^-6: subnormal steps of 2^-9 */
+    const float m = rintf(a * 512.0f);     /* exact scaling; rint = ties to even */
+    return sign | (uint8_t)m;              /* m == 8 is the smallest normal, 0x08 */
+  }
+  int e;
+  const float f = frexpf(a, &e);           /* a = f * 2^e, f in [0.5, 1) */
+  const float mm = rintf((f * 2.0f - 1.0f) * 8.0f);  /* 3 mantissa bits, exact operands */
+  int ex = e - 1 + 7, man = (int)mm;
+  if (man == 8) {
+    man = 0;
+    ++ex;
+  }
+  return sign | (uint8_t)((ex << 3) | man);
+}
+
+float oracle_e4m3_to_f32(uint8_t q) {
+  const int e = (q >> 3) & 15, m = q & 7;
+  const float a = e == 0 ? ldexpf((float)m, -9) : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+  return (q & 0x80) ? -a : a;
+}
+
+/* src [nmat, rows, K] (fp32 or bf16) -> q [nmat, rows, K] E4M3 bytes and
+ * s [nmat, rows / block_rows, K / 128] fp32 scales (blocks of block_rows x
+ * 128; block_rows = 128 for weights, 1 for activations). */
+void oracle_quantize_fp8(const void *src, int dt, int64_t nmat, int rows, int K, int block_rows,
+                         uint8_t *q, float *s) {
+  const int nrb = rows / block_rows, nkb = K / 128;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nmat * nrb * nkb; ++b) {
+    const int64_t m = b / ((int64_t)nrb * nkb);
+    const int rb = (int)((b / nkb) % nrb), kb = (int)(b % nkb);
+    float amax = 0.0f;
+    for (int r = rb * block_rows; r < (rb + 1) * block_rows; ++r)
+      for (int c = kb * 128; c < (kb + 1) * 128; ++c) {
+        const float a = fabsf(orc_ld(src, (m * rows + r) * (int64_t)K + c, dt));
+        amax = a > amax ? a : amax;
+      }
+    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    s[b] = scale;
+    for (int r = rb * block_rows; r < (rb + 1) * block_rows; ++r)
+      for (int c = kb * 128; c < (kb + 1) * 128; ++c) {
+        const int64_t i = (m * rows + r) * (int64_t)K + c;
+        q[i] = oracle_e4m3_from_f32(orc_ld(src, i, dt) / scale);
+      }
+  }
+}
+
+/* One row of a block-scaled GEMM: sum over K blocks of
+ * (sa[kb] * sb[kb]) * (sum of the quantized products in the block). */
+static float orc_dot_fp8(int K, const uint8_t *qa, const float *sa, const uint8_t *qb,
+                         const float *sb) {
+  float acc = 0.0f;
+  for (int kb = 0; kb < K / 128; ++kb) {
+    float blk = 0.0f;
+    for (int c = kb * 128; c < (kb + 1) * 128; ++c)
+      blk += oracle_e4m3_to_f32(qa[c]) * oracle_e4m3_to_f32(qb[c]);
+    const float sc = sa[kb] * sb[kb];
+    acc += blk * sc;
+  }
+  return acc;
+}
+
+/* Quantize one fp32 row of K (multiple of 128) per [1,128] block. */
+static void orc_quant_row(int K, const float *v, uint8_t *q, float *s) {
+  for (int kb = 0; kb < K / 128; ++kb) {
+    float amax = 0.0f;
+    for (int c = kb * 128; c < (kb + 1) * 128; ++c) amax = fabsf(v[c]) > amax ? fabsf(v[c]) : amax;
+    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    s[kb] = scale;
+    for (int c = kb * 128; c < (kb + 1) * 128; ++c) q[c] = oracle_e4m3_from_f32(v[c] / scale);
+  }
+}
+
+/* One FFN expert on a quantized token: g, u (block-scaled GEMMs against
+ * W_gate/W_up, scales [I/128, d/128]), h = silu(g) * u, h quantized per
+ * [1,128], y = block-scaled GEMM against W_down (scales [d/128, I/128]). */
+static void orc_expert_fp8(int d, int I, const uint8_t *qx, const float *sx, const uint8_t *qwg,
+                           const float *swg, const uint8_t *qwu, const float *swu,
+                           const uint8_t *qwd, const float *swd, float *h, uint8_t *qh,
+                           float *sh, float *y) {
+  const int dkb = d / 128, ikb = I / 128;
+  for (int r = 0; r < I; ++r) {
+    const float g = orc_dot_fp8(d, qwg + (int64_t)r * d, swg + (int64_t)(r / 128) * dkb, qx, sx);
+    const float u = orc_dot_fp8(d, qwu + (int64_t)r * d, swu + (int64_t)(r / 128) * dkb, qx, sx);
+    h[r] = (g / (1.0f + expf(-g))) * u;
+  }
+  orc_quant_row(I, h, qh, sh);
+  for (int i = 0; i < d; ++i)
+    y[i] = orc_dot_fp8(I, qwd + (int64_t)i * I, swd + (int64_t)(i / 128) * ikb, qh, sh);
+}
+
+/* Steps 3-5 for one token with given routing, FP8 experts.  Pointer arrays
+ * hold, per slot j, the expert's quantized matrices and scales (unused for
+ * zero slots).  x_row in the inputs' dtype; out: d floats. */
+void oracle_token_output_fp8(int d, int I, int N, int k, const void *x_row, int dt,
+                             const int32_t *idx, const float *gate, const uint8_t *const *qwg,
+                             const float *const *swg, const uint8_t *const *qwu,
+                             const float *const *swu, const uint8_t *const *qwd,
+                             const float *const *swd, float *out) {
+  float *x = (float *)malloc(sizeof(float) * (size_t)d);
+  uint8_t *qx = (uint8_t *)malloc((size_t)d);
+  float *sx = (float *)malloc(sizeof(float) * (size_t)(d / 128));
+  float *h = (float *)malloc(sizeof(float) * (size_t)(I > 0 ? I : 1));
+  uint8_t *qh = (uint8_t *)malloc((size_t)(I > 0 ? I : 1));
+  float *sh = (float *)malloc(sizeof(float) * (size_t)(I / 128 > 0 ? I / 128 : 1));
+  float *y = (float *)malloc(sizeof(float) * (size_t)d);
+  for (int c = 0; c < d; ++c) x[c] = orc_ld(x_row, c, dt);
+  orc_quant_row(d, x, qx, sx);
+  float zsum = 0.0f;
+  for (int j = 0; j < k; ++j)
+    if (idx[j] >= N) zsum += gate[j];
+  for (int c = 0; c < d; ++c) out[c] = zsum * x[c];
+  for (int j = 0; j < k; ++j) {
+    if (idx[j] >= N) continue;
+    orc_expert_fp8(d, I, qx, sx, qwg[j], swg[j], qwu[j], swu[j], qwd[j], swd[j], h, qh, sh, y);
+    for (int c = 0; c < d; ++c) out[c] += gate[j] * y[c];
+  }
+  free(x);
+  free(qx);
+  free(sx);
+  free(h);
+  free(qh);
+  free(sh);
+  free(y);
+}
+
+/* All tokens with given routing; weights q [N, rows, K] with scales
+ * [N, rows/128, K/128] (W_gate/W_up rows I, K d; W_down rows d, K I). */
+void oracle_combine_given_routing_fp8(int64_t T, int d, int I, int N, int k, const void *x, int dt,
+                                      const int32_t *idx, const float *gate, const uint8_t *qwg,
+                                      const float *swg, const uint8_t *qwu, const float *swu,
+                                      const uint8_t *qwd, const float *swd, float *out) {
+  const size_t es = dt == ORC_F32 ? 4 : 2;
+  const size_t per = (size_t)I * (size_t)d, sper = (size_t)(I / 128) * (size_t)(d / 128);
+#pragma omp parallel
+  {
+    const uint8_t **pg = (const uint8_t **)malloc(sizeof(void *) * (size_t)k);
+    const uint8_t **pu = (const uint8_t **)malloc(sizeof(void *) * (size_t)k);
+    const uint8_t **pd = (const uint8_t **)malloc(sizeof(void *) * (size_t)k);
+    const float **sg = (const float **)malloc(sizeof(void *) * (size_t)k);
+    const float **su = (const float **)malloc(sizeof(void *) * (size_t)k);
+    const float **sd = (const float **)malloc(sizeof(void *) * (size_t)k);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[t * k + j];
+        const int ffn = e < N;
+        pg[j] = ffn ? qwg + (size_t)e * per : NULL;
+        pu[j] = ffn ? qwu + (size_t)e * per : NULL;
+        pd[j] = ffn ? qwd + (size_t)e * per : NULL;
+        sg[j] = ffn ? swg + (size_t)e * sper : NULL;
+        su[j] = ffn ? swu + (size_t)e * sper : NULL;
+        sd[j] = ffn ? swd + (size_t)e * sper : NULL;
+      }
+      oracle_token_output_fp8(d, I, N, k, (const char *)x + (size_t)t * (size_t)d * es, dt,
+                              idx + t * k, gate + t * k, pg, sg, pu, su, pd, sd,
+                              out + t * (int64_t)d);
+    }
+    free(pg);
+    free(pu);
+    free(pd);
+    free(sg);
+    free(su);
+    free(sd);
+  }
+}
+
+/* The whole FP8-expert forward: routing as in oracle_forward, then the
+ * block-scaled experts. */
+void oracle_forward_fp8(int64_t T, int d, int I, int N, int Z, int k, int dt, const void *x,
+                        const void *w_router, const float *bias, const uint8_t *qwg,
+                        const float *swg, const uint8_t *qwu, const float *swu,
+                        const uint8_t *qwd, const float *swd, float *out, int32_t *counts,
+                        int32_t *idx, float *gate, float *margin) {
+  int E = N + Z;
+  float *logits = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * (size_t)E);
+  oracle_router_logits(T, d, E, x, w_router, dt, logits);
+  oracle_route_from_logits(T, E, k, logits, bias, idx, gate, margin, NULL);
+  oracle_counts(T, k, E, idx, counts);
+  oracle_combine_given_routing_fp8(T, d, I, N, k, x, dt, idx, gate, qwg, swg, qwu, swu, qwd, swd,
+                                   out);
+  free(logits);
+}
