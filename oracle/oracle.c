@@ -273,8 +273,13 @@ void oracle_bias_update(int E, int64_t T, const int32_t *counts, const float *ta
  *   - FP8 = OCP E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits,
  *     subnormals, largest finite 448, no infinities;
  *   - conversion rounds to nearest, ties to even, and saturates at +-448;
- *   - a block's scale is amax / 448 (1 for an all-zero block), q = E4M3(v /
- *     scale), so the block's largest magnitude maps to 448;
+ *   - a block's scale is a power of two, the smallest 2^e >= amax / 448
+ *     (e >= -127; 1 for an all-zero block), and q = E4M3(v / scale), so the
+ *     block's largest magnitude lands in (224, 448] and dividing by the
+ *     scale is exact.  (DeepSeek-V3 keeps fp32 scales; a power-of-two scale
+ *     is one exponent byte per block, which the gfx950 FP8 matrix
+ *     instructions apply in hardware, and loses at most one bit of the
+ *     block's range.);
  *   - a GEMM adds, per 128-wide K block, (scale_a * scale_b) times the fp32
  *     sum of the products of the quantized values;
  *   - the router stays in the inputs' dtype; x is quantized per [1,128]
@@ -308,6 +313,17 @@ float oracle_e4m3_to_f32(uint8_t q) {
   return (q & 0x80) ? -a : a;
 }
 
+/* Block scale: the smallest power of two >= amax / 448, not below 2^-127;
+ * 1 when amax is 0. */
+static float orc_block_scale(float amax) {
+  if (!(amax > 0.0f)) return 1.0f;
+  int E;
+  const float f = frexpf(amax / 448.0f, &E); /* r = f * 2^E, f in [0.5, 1) */
+  int e = f == 0.5f ? E - 1 : E;
+  if (e < -127) e = -127;
+  return ldexpf(1.0f, e);
+}
+
 /* src [nmat, rows, K] (fp32 or bf16) -> q [nmat, rows, K] E4M3 bytes and
  * s [nmat, rows / block_rows, K / 128] fp32 scales (blocks of block_rows x
  * 128; block_rows = 128 for weights, 1 for activations). */
@@ -324,7 +340,7 @@ void oracle_quantize_fp8(const void *src, int dt, int64_t nmat, int rows, int K,
         const float a = fabsf(orc_ld(src, (m * rows + r) * (int64_t)K + c, dt));
         amax = a > amax ? a : amax;
       }
-    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const float scale = orc_block_scale(amax);
     s[b] = scale;
     for (int r = rb * block_rows; r < (rb + 1) * block_rows; ++r)
       for (int c = kb * 128; c < (kb + 1) * 128; ++c) {
@@ -354,7 +370,7 @@ static void orc_quant_row(int K, const float *v, uint8_t *q, float *s) {
   for (int kb = 0; kb < K / 128; ++kb) {
     float amax = 0.0f;
     for (int c = kb * 128; c < (kb + 1) * 128; ++c) amax = fabsf(v[c]) > amax ? fabsf(v[c]) : amax;
-    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const float scale = orc_block_scale(amax);
     s[kb] = scale;
     for (int c = kb * 128; c < (kb + 1) * 128; ++c) q[c] = oracle_e4m3_from_f32(v[c] / scale);
   }

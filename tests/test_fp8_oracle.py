@@ -3,8 +3,8 @@
 The pages ask for DeepSeek-V3-style fine-grained quantization: activations
 per [1,128] block, weights per [128,128] block (LongCat-Flash summary,
 section 6, custom kernels).  The format (OCP E4M3), the rounding (nearest,
-ties to even, saturating) and the scale rule (amax/448) are this project's
-readings; these tests tie the oracle to torch's float8_e4m3fn cast (a
+ties to even, saturating) and the scale rule (the smallest power of two >=
+amax/448) are this project's readings; these tests tie the oracle to torch's float8_e4m3fn cast (a
 library routine), to the format's arithmetic, to a float64 re-derivation of
 the block-scaled forward and to the closed forms of the zero-expert paths."""
 import numpy as np
@@ -55,9 +55,10 @@ def test_saturates_at_448():
 
 @pytest.mark.parametrize("block_rows", [128, 1])
 def test_block_quantization(block_rows):
-    """Each block's largest magnitude maps to 448; every value is within half
-    a step of the grid; the bytes equal torch's cast of v / scale; an
-    all-zero block gets scale 1 and zeros."""
+    """Each block's scale is the smallest power of two >= amax/448, so its
+    scaled largest magnitude lies in (224, 448]; every value is within half a step
+    of the grid; the bytes equal torch's cast of v / scale; an all-zero
+    block gets scale 1 and zeros."""
     rng = np.random.default_rng(block_rows)
     w = (rng.standard_normal((2, 256, 384)) * rng.choice([1e-3, 1.0, 30.0], (2, 256, 1)))
     w = w.astype(np.float32)
@@ -75,8 +76,12 @@ def test_block_quantization(block_rows):
                 if amax == 0:
                     assert sc == 1.0 and (q[blk] == 0).all()
                     continue
-                assert sc == np.float32(amax) / np.float32(448.0)
-                assert (np.abs(deq[blk]) == 448.0).any()
+                r = np.float32(amax) / np.float32(448.0)
+                mant, _ = np.frexp(sc)
+                assert mant == 0.5 and sc >= r and sc / 2 < r  # power of two, smallest >= r
+                assert 224.0 < amax / sc <= 448.0
+                top = np.abs(deq[blk]).max()
+                assert 224.0 <= top <= 448.0  # the scaled maximum may round down to 224
                 ref = torch_e4m3(v / np.float32(sc))
                 assert (q[blk] == ref).all()
                 err = np.abs(deq[blk] * sc - v)
@@ -90,7 +95,9 @@ def _quant_rows_f64(v):
     for kb in range(v.shape[-1] // 128):
         blk = v[..., kb * 128:(kb + 1) * 128]
         amax = np.abs(blk).max(axis=-1, keepdims=True)
-        sc = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        r = (amax / np.float32(448.0)).astype(np.float32)
+        sc = np.where(amax > 0, 2.0 ** np.ceil(np.log2(np.where(r > 0, r, 1.0).astype(np.float64))),
+                      1.0).astype(np.float32)
         q = torch.from_numpy((blk / sc).astype(np.float32)).to(torch.float8_e4m3fn).float().numpy()
         out[..., kb * 128:(kb + 1) * 128] = q.astype(np.float64) * sc
     return out
