@@ -23,6 +23,7 @@ METRIC = "MoE-layer tokens/s at 1 MI355X; % bf16 MFMA peak (prefill) / % HBM BW 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # dense fp8
 
 
 def parse():
@@ -33,24 +34,30 @@ def parse():
     ap.add_argument("--workload", default="prod", choices=["prod", "decode", "small", "skewed", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: auto)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="block-scaled FP8 experts (moe_zc_forward_fp8); a separate line, "
+                         "not the bf16 headline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
-def algorithmic(cfg, counts):
-    """Algorithmic FLOPs and HBM bytes of one step, and of each expert GEMM."""
+def algorithmic(cfg, counts, fp8=False):
+    """Algorithmic FLOPs and HBM bytes of one step, and of each expert GEMM
+    (fp8: expert weights and their activations one byte per element, plus
+    one exponent byte per 128 x 128 weight block)."""
     import numpy as np
 
     s = 2 if cfg.dtype == "bf16" else 4
+    ws = 1 if fp8 else s
     cnt = np.asarray(counts, dtype=np.int64)
     P = int(cnt[: cfg.N].sum())
     touched = int((cnt[: cfg.N] > 0).sum())
     T, d, I, E, k = cfg.T, cfg.d, cfg.I, cfg.E, cfg.k
-    per_expert = d * I * s
+    per_expert = d * I * ws + (d * I // (128 * 128) if fp8 else 0)
     step_bytes = (T * d * s * 2 + E * d * s + touched * 3 * per_expert + E * 8 + T * k * 8)
     step_flops = 6 * d * I * P + 2 * d * E * T
-    gate_up = {"bytes": touched * 2 * per_expert + T * d * s, "flops": 4 * d * I * P}
+    gate_up = {"bytes": touched * 2 * per_expert + T * d * ws, "flops": 4 * d * I * P}
     down = {"bytes": touched * per_expert, "flops": 2 * d * I * P}
     router = {"bytes": T * d * s + E * d * s, "flops": 2 * d * E * T}
     return {"P": P, "touched": touched, "step_bytes": step_bytes, "step_flops": step_flops,
@@ -159,18 +166,33 @@ def main():
     print(f"[bench] inputs for {cfg.name} generated on device in {time.time() - t0:.1f}s",
           file=sys.stderr, flush=True)
     dt_code = moe.BF16 if cfg.dtype == "bf16" else moe.F32
-    nbytes = moe.workspace_bytes(cfg.T, cfg.d, cfg.I, cfg.N, cfg.Z, cfg.k, dt_code)
+    if args.fp8:
+        # quantize the expert weights once, untimed ([128,128] blocks), and
+        # drop the bf16 copies
+        q = {}
+        for w in ("W_gate", "W_up", "W_down"):
+            q[w], q[w + "_exp"] = moe.quantize_fp8(inp[w], 128)
+            inp[w] = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        nbytes = moe.workspace_bytes_fp8(cfg.T, cfg.d, cfg.I, cfg.N, cfg.Z, cfg.k)
+        fwd = moe.forward_fp8
+        args_fwd = (inp["x"], inp["W_router"], inp["bias"], q["W_gate"], q["W_gate_exp"],
+                    q["W_up"], q["W_up_exp"], q["W_down"], q["W_down_exp"], cfg.N, cfg.Z, cfg.k)
+    else:
+        nbytes = moe.workspace_bytes(cfg.T, cfg.d, cfg.I, cfg.N, cfg.Z, cfg.k, dt_code)
+        fwd = moe.forward
+        args_fwd = (inp["x"], inp["W_router"], inp["bias"], inp["W_gate"], inp["W_up"],
+                    inp["W_down"], cfg.N, cfg.Z, cfg.k)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["x"])
     counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
     idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
     gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
-    args_fwd = (inp["x"], inp["W_router"], inp["bias"], inp["W_gate"], inp["W_up"], inp["W_down"],
-                cfg.N, cfg.Z, cfg.k)
     kw = dict(out=out, counts=counts, topk_idx=idx, topk_gate=gate, workspace=ws)
 
     for _ in range(args.warmup):
-        moe.forward(*args_fwd, **kw)
+        fwd(*args_fwd, **kw)
     torch.cuda.synchronize()
     timer = moe.Timer(max(1, args.steps))
     stream = torch.cuda.current_stream(dev)
@@ -178,7 +200,7 @@ def main():
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
-        moe.forward(*args_fwd, **kw, timer=timer)
+        fwd(*args_fwd, **kw, timer=timer)
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
@@ -189,25 +211,30 @@ def main():
     print(f"[bench] {args.steps} steps: {ms:.3f} ms/step; stages " +
           " ".join(f"{k}={v:.3f}" for k, v in stage_avg.items()), file=sys.stderr, flush=True)
 
-    alg = algorithmic(cfg, counts.cpu().numpy())
+    alg = algorithmic(cfg, counts.cpu().numpy(), fp8=args.fp8)
     gu_s = stage_avg["gate_up"] / 1e3
     dn_s = stage_avg["down"] / 1e3
     rt_s = stage_avg["router"] / 1e3
     peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    expert_peak_tf = MFMA_FP8_PEAK_TFLOPS if args.fp8 else peak_tf
     gu_gbs = alg["gate_up"]["bytes"] / gu_s / 1e9
-    roofline = {"bound": "hbm", "kernel": "gemm_kernel<bf16,GATE_UP> (gate/up GEMM + SwiGLU)",
+    kname = ("gemm8_kernel<GATE_UP> (FP8 gate/up GEMM + SwiGLU + [1,128] quantization of H)"
+             if args.fp8 else "gemm_kernel<bf16,GATE_UP> (gate/up GEMM + SwiGLU)")
+    roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
+                "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None if args.fp8 else measured_traffic(cfg.name),
                 "algorithmic_bytes_per_launch": alg["gate_up"]["bytes"],
                 "avg_launch_ms": round(stage_avg["gate_up"], 4)}
     kernels = {}
     for name, sec in (("router", rt_s), ("gate_up", gu_s), ("down", dn_s)):
         a = alg[name]
+        pk = peak_tf if name == "router" else expert_peak_tf
         kernels[name] = {"ms": round(sec * 1e3, 4),
                          "GB/s": round(a["bytes"] / sec / 1e9, 1),
                          "TFLOP/s": round(a["flops"] / sec / 1e12, 1),
                          "hbm_frac": round(a["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4),
-                         "mfma_frac": round(a["flops"] / sec / 1e12 / peak_tf, 4)}
+                         "mfma_frac": round(a["flops"] / sec / 1e12 / pk, 4)}
     step_s = ms / 1e3
     res = {
         "metric": METRIC,
@@ -220,15 +247,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": ("fp8-e4m3 experts ([128,128] weight / [1,128] activation power-of-two "
+                  "block scales), bf16 router and activations") if args.fp8 else cfg.dtype,
         "data": "synthetic (seeded Philox4x64 normals; random-init weights)",
         "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} I={cfg.I} N={cfg.N} Z={cfg.Z} "
-                               f"k={cfg.k} {cfg.dtype}",
+                               f"k={cfg.k} {cfg.dtype}" + (", FP8 experts" if args.fp8 else ""),
                    "T": cfg.T, "d": cfg.d, "I": cfg.I, "N": cfg.N, "Z": cfg.Z, "k": cfg.k,
                    "ffn_pairs": alg["P"], "touched_experts": alg["touched"]},
         "roofline": roofline,
         "step_hbm_frac": round(alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
-        "step_mfma_frac": round(alg["step_flops"] / step_s / 1e12 / peak_tf, 4),
+        "step_mfma_frac": round(alg["step_flops"] / step_s / 1e12 / expert_peak_tf, 4),
         "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
         "kernels": kernels,
     }
@@ -247,7 +275,7 @@ def main():
     bu_us = ev0.elapsed_time(ev1) / 200 * 1e3
     res["bias_update"] = {"us_per_call": round(bu_us, 2), "experts": cfg.E,
                           "bytes_per_call": cfg.E * 32, "bound": "launch latency"}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.fp8:  # the oracle baseline is the bf16 path's
         ntok = args.cpu_tokens or {"prod": 1536, "skewed": 1536, "decode": 128, "small": 4096,
                                    "tiny": 64}[cfg.name]
         res["cpu_baseline"] = cpu_baseline(cfg, inp, min(ntok, cfg.T))

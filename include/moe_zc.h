@@ -174,6 +174,57 @@ void moe_zc_timer_reset(moe_zc_timer *timer);
 
 void moe_zc_timer_destroy(moe_zc_timer *timer);
 
+/* ------------------------------------------------------------------------
+ * Block-scaled FP8 experts.
+ *
+ * LongCat-Flash technical-report summary page, section 6 "inference and
+ * deployment", custom kernels, quantization item: fine-grained block
+ * quantization as in DeepSeek-V3, activations per [1,128] block and weights
+ * per [128,128] block.  This library's reading: values are OCP E4M3 bytes
+ * (round to nearest even, saturating at 448), and every block has one
+ * power-of-two scale 2^e, the smallest with 2^e >= amax / 448 (e >= -127;
+ * e = 0 for an all-zero block), stored as the E8M0 byte e + 127.  The expert
+ * GEMMs add, per 128-wide K block, 2^(e_a + e_b) times the fp32 sum of the
+ * products of the E4M3 values.  The router stays bfloat16; x is quantized
+ * per [1,128] before the gate/up projections and the SwiGLU activations per
+ * [1,128] before the down projection; zero experts return the unquantized
+ * x; expert outputs are bfloat16 and the combine is as in moe_zc_forward.
+ * ------------------------------------------------------------------------ */
+
+/* Quantizes nmat row-major [rows, K] matrices (src: fp32 or bf16 per
+ * `dtype`) into q (same shape, E4M3 bytes) and scale_exp
+ * [nmat, rows / block_rows, K / 128] (E8M0 bytes).  block_rows = 128 for
+ * weights ([128,128] blocks), 1 for activations ([1,128] blocks).  Device
+ * pointers, src and q 16-byte aligned; asynchronous on `stream`.
+ * MOE_ZC_EDTYPE for another dtype; MOE_ZC_EINVAL for negative sizes, a
+ * block_rows other than 1 or 128, or a NULL pointer with non-empty input;
+ * MOE_ZC_EALIGN if rows is not a multiple of block_rows, K not a multiple
+ * of 128, or a pointer is misaligned.  Empty input: MOE_ZC_OK, nothing
+ * enqueued. */
+int moe_zc_quantize_fp8(const void *src, int32_t dtype, int64_t nmat, int32_t rows, int32_t K,
+                        int32_t block_rows, uint8_t *q, uint8_t *scale_exp, void *stream);
+
+/* Workspace bytes of moe_zc_forward_fp8 for `dims` (0 for invalid dims). */
+size_t moe_zc_workspace_bytes_fp8(const moe_zc_dims *dims);
+
+/* The forward pass with FP8 experts: as moe_zc_forward, with
+ *   dims->dtype   MOE_ZC_BF16 (x, W_router, out); d and I multiples of 128,
+ *                 at most 12288
+ *   W_gate, W_up  [N, I, d] E4M3, exponents W_*_exp [N, I/128, d/128]
+ *   W_down        [N, d, I] E4M3, exponents W_down_exp [N, d/128, I/128]
+ *                 (as produced by moe_zc_quantize_fp8 with block_rows 128)
+ *   timer         nullable; as in moe_zc_forward_timed (the activation
+ *                 quantization is timed with MOE_ZC_STAGE_PERMUTE)
+ * MOE_ZC_EDTYPE unless dims->dtype is MOE_ZC_BF16; MOE_ZC_EALIGN if d or I
+ * is not a multiple of 128; MOE_ZC_EINVAL if either exceeds 12288; other
+ * errors as moe_zc_forward. */
+int moe_zc_forward_fp8(const moe_zc_dims *dims, const void *x, const void *W_router,
+                       const float *bias, const uint8_t *W_gate, const uint8_t *W_gate_exp,
+                       const uint8_t *W_up, const uint8_t *W_up_exp, const uint8_t *W_down,
+                       const uint8_t *W_down_exp, void *out, int32_t *counts, int32_t *topk_idx,
+                       float *topk_gate, void *workspace, size_t workspace_bytes, void *stream,
+                       moe_zc_timer *timer);
+
 #ifdef __cplusplus
 }
 #endif

@@ -158,3 +158,47 @@ def bias_call(E=16, T=64, counts=A, target=2 * A, bias=3 * A, state=None, lr=0.1
 ])
 def test_bias_update_rejects(kw, expect):
     assert bias_call(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dtype=5), EDTYPE),
+    (dict(block_rows=64), EINVAL),
+    (dict(rows=-1), EINVAL),
+    (dict(K=200), EALIGN),
+    (dict(rows=130), EALIGN),
+    (dict(q=None), EINVAL),
+    (dict(s=None), EINVAL),
+    (dict(src=A + 8), EALIGN),
+])
+def test_quantize_fp8_rejects(kw, expect):
+    a = dict(src=A, dtype=moe.BF16, nmat=2, rows=256, K=384, block_rows=128, q=2 * A, s=3 * A)
+    a.update(kw)
+    st = moe.lib().moe_zc_quantize_fp8(a["src"], a["dtype"], a["nmat"], a["rows"], a["K"],
+                                       a["block_rows"], a["q"], a["s"], None)
+    assert st == expect
+
+
+def test_quantize_fp8_empty_is_ok():
+    assert moe.lib().moe_zc_quantize_fp8(None, moe.BF16, 0, 128, 128, 128, None, None, None) == 0
+
+
+def fp8_call(dims, exps=(9 * A, 10 * A, 11 * A), ws_bytes=None, **kw):
+    lib = moe.lib()
+    if ws_bytes is None:
+        ws_bytes = lib.moe_zc_workspace_bytes_fp8(ctypes.byref(dims))
+    st = lib.moe_zc_forward_fp8(ctypes.byref(dims), A, 2 * A, 3 * A, 4 * A, exps[0], 5 * A, exps[1],
+                                6 * A, exps[2], 7 * A, 8 * A, None, None, 16 * A, ws_bytes, None,
+                                None)
+    assert st != 0, "a test call passed validation: it would have launched work"
+    return st
+
+
+def test_forward_fp8_rejects():
+    assert fp8_call(D(T=64, d=256, I=128, dtype=moe.F32)) == EDTYPE
+    assert fp8_call(D(T=64, d=200, I=128)) == EALIGN
+    assert fp8_call(D(T=64, d=256, I=72)) == EALIGN
+    assert fp8_call(D(T=64, d=256, I=128), exps=(9 * A, None, 11 * A)) == EINVAL
+    assert fp8_call(D(T=64, d=256, I=128), ws_bytes=100) == ENOSPC
+    assert moe.lib().moe_zc_workspace_bytes_fp8(ctypes.byref(D(T=64, d=200, I=128))) == 0
+    assert (moe.lib().moe_zc_workspace_bytes_fp8(ctypes.byref(D(T=4096, d=256, I=128)))
+            > moe.lib().moe_zc_workspace_bytes_fp8(ctypes.byref(D(T=64, d=256, I=128))))

@@ -21,7 +21,8 @@ STATUS = {0: "MOE_ZC_OK", -1: "MOE_ZC_EINVAL", -2: "MOE_ZC_EDTYPE", -3: "MOE_ZC_
 STAGES = ("router", "topk", "scan", "permute", "gate_up", "down", "combine")
 EXPORTS = ("moe_zc_workspace_bytes", "moe_zc_forward", "moe_zc_status_string",
            "moe_zc_timer_create", "moe_zc_forward_timed", "moe_zc_timer_read",
-           "moe_zc_timer_reset", "moe_zc_timer_destroy", "moe_zc_bias_update")
+           "moe_zc_timer_reset", "moe_zc_timer_destroy", "moe_zc_bias_update",
+           "moe_zc_quantize_fp8", "moe_zc_workspace_bytes_fp8", "moe_zc_forward_fp8")
 
 
 class MoeZcError(RuntimeError):
@@ -66,6 +67,14 @@ def lib():
         L.moe_zc_timer_reset.argtypes = [vp]
         L.moe_zc_timer_destroy.restype = None
         L.moe_zc_timer_destroy.argtypes = [vp]
+        L.moe_zc_quantize_fp8.restype = ctypes.c_int
+        L.moe_zc_quantize_fp8.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+        L.moe_zc_workspace_bytes_fp8.restype = sz
+        L.moe_zc_workspace_bytes_fp8.argtypes = [dims_p]
+        L.moe_zc_forward_fp8.restype = ctypes.c_int
+        L.moe_zc_forward_fp8.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, sz, vp, vp]
         f32 = ctypes.c_float
         L.moe_zc_bias_update.restype = ctypes.c_int
         L.moe_zc_bias_update.argtypes = [ctypes.c_int32, ctypes.c_int64, vp, vp, vp, vp, f32, f32,
@@ -194,3 +203,68 @@ def bias_update(counts, target, bias, T: int, lr: float, ki: float = 1.0, kp: fl
                                     _ptr(state), float(lr), float(ki), float(kp), float(kd),
                                     int(mode), stream))
     return bias, state
+
+
+# ---------------------------------------------------------------------------
+# Block-scaled FP8 experts
+# ---------------------------------------------------------------------------
+
+def quantize_fp8(src, block_rows: int, q=None, scale_exp=None, stream=None):
+    """moe_zc_quantize_fp8 on a torch device tensor [nmat, rows, K] or
+    [rows, K] (float32 or bfloat16): returns (q uint8, same shape;
+    scale_exp uint8 [nmat, rows/block_rows, K/128] or [rows/block_rows, K/128])."""
+    import torch
+
+    shape = tuple(src.shape)
+    nmat, rows, K = (1,) + shape if len(shape) == 2 else shape
+    if q is None:
+        q = torch.empty(shape, dtype=torch.uint8, device=src.device)
+    if scale_exp is None:
+        sshape = (rows // block_rows, K // 128)
+        scale_exp = torch.empty(sshape if len(shape) == 2 else (nmat,) + sshape,
+                                dtype=torch.uint8, device=src.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device).cuda_stream
+    _check(lib().moe_zc_quantize_fp8(_ptr(src), _dtype_code(src), int(nmat), int(rows), int(K),
+                                     int(block_rows), _ptr(q), _ptr(scale_exp), stream))
+    return q, scale_exp
+
+
+def workspace_bytes_fp8(T, d, I, N, Z, k) -> int:
+    return int(lib().moe_zc_workspace_bytes_fp8(ctypes.byref(make_dims(T, d, I, N, Z, k, BF16))))
+
+
+def forward_fp8(x, W_router, bias, W_gate, W_gate_exp, W_up, W_up_exp, W_down, W_down_exp,
+                N: int, Z: int, k: int, *, out=None, counts=None, topk_idx=None, topk_gate=None,
+                workspace=None, stream=None, timer: Optional[Timer] = None,
+                want_routing: bool = True):
+    """moe_zc_forward_fp8 on torch device tensors: x, W_router bfloat16; the
+    expert matrices E4M3 bytes (uint8) with E8M0 exponents as returned by
+    quantize_fp8(W, 128).  Returns (out, counts, topk_idx, topk_gate)."""
+    import torch
+
+    T, d = x.shape
+    I = W_gate.shape[1] if (W_gate is not None and N > 0) else 0
+    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x))
+    dev = x.device
+    if out is None:
+        out = torch.empty_like(x)
+    if counts is None:
+        counts = torch.empty(N + Z, dtype=torch.int32, device=dev)
+    if want_routing:
+        if topk_idx is None:
+            topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        if topk_gate is None:
+            topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        nbytes = int(lib().moe_zc_workspace_bytes_fp8(ctypes.byref(dims)))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(lib().moe_zc_forward_fp8(
+        ctypes.byref(dims), _ptr(x), _ptr(W_router), _ptr(bias), _ptr(W_gate), _ptr(W_gate_exp),
+        _ptr(W_up), _ptr(W_up_exp), _ptr(W_down), _ptr(W_down_exp), _ptr(out), _ptr(counts),
+        _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), stream,
+        timer.handle if timer is not None else None))
+    return out, counts, topk_idx, topk_gate

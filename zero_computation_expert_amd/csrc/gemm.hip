@@ -40,40 +40,9 @@
 //     (workgroups are dealt round-robin over the 8 XCDs): the row blocks of
 //     one expert share that expert's token rows in one L2, and the chunks of
 //     one row block share its weight rows.
-#include <algorithm>
-#include <type_traits>
-
-#include "moe_zc_internal.h"
+#include "gemm_common.h"
 
 namespace moezc {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-enum { MODE_ROUTER = 0, MODE_GATE_UP = 1, MODE_DOWN = 2 };
-
-struct GemmArgs {
-  const void *wa;   // ROUTER: W_router; GATE_UP: W_gate; DOWN: W_down
-  const void *wb;   // GATE_UP: W_up
-  const void *src;  // token rows: x (ROUTER, GATE_UP) or H (DOWN)
-  const int32_t *tok;        // GATE_UP: token of each permuted row
-  const int32_t *offs;       // [N+1] permuted row offsets (GATE_UP, DOWN)
-  const int32_t *chunk_off;  // [N+1] chunk prefix (GATE_UP, DOWN)
-  const int32_t *meta;       // meta[0] = total chunks (GATE_UP, DOWN)
-  void *out;                 // logits (f32) / H / Y
-  int64_t w_expert_stride;   // elements between experts' matrices
-  int64_t T;                 // tokens (ROUTER: chunking; GATE_UP: rows of x)
-  int K;                     // reduction length
-  int nrows;                 // weight rows per expert (E, I or d)
-  int out_ld;                // elements per output row
-  int nrb;                   // row blocks per chunk
-  int N;                     // FFN experts (GATE_UP, DOWN)
-  int split;                 // ROUTER: K slices (1 = no split)
-  int kslice;                // ROUTER: K elements per slice
-  int64_t part_stride;       // ROUTER: elements between slices' partial logits
-};
 
 template <typename T>
 struct MfmaOps;
@@ -102,116 +71,6 @@ struct MfmaOps<float> {
   }
 };
 
-template <typename T>
-__device__ __forceinline__ void store4(T *dst, float a, float b, float c, float d);
-template <>
-__device__ __forceinline__ void store4<float>(float *dst, float a, float b, float c, float d) {
-  *reinterpret_cast<float4 *>(dst) = make_float4(a, b, c, d);
-}
-template <>
-__device__ __forceinline__ void store4<bf16_t>(bf16_t *dst, float a, float b, float c, float d) {
-  uint2 v;
-  v.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-  v.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
-  *reinterpret_cast<uint2 *>(dst) = v;
-}
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
-constexpr int kThreads = 256;                  // 4 waves, each with two 32-row weight blocks
-constexpr int kWaveRowBytes = 64 * 128;        // one K-step of a wave's 64 weight rows
-constexpr int kWSlotBytes = 4 * kWaveRowBytes; // one K-step of the workgroup's weights
-constexpr int kPitch = 128;  // LDS bytes per token row (16-byte chunks XOR-swizzled by row)
-constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: the load reads zeros
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
-}
-
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(off), 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Per-thread state of one tile.
-template <int NB>
-struct TileState {
-  __amdgpu_buffer_rsrc_t ra[2];  // weight matrix of each 32-row block (A operand)
-  __amdgpu_buffer_rsrc_t rb;     // token rows (B operand)
-  uint32_t wrow[2][4];           // byte offset of the weight row this lane loads in each
-                                 // direct-to-LDS instruction (block, 8-row group)
-  uint32_t wchunk;               // byte offset of the 16-byte chunk this lane loads
-  int wkpos;                     // K element of that chunk within a step
-  uint32_t vob[NB];              // byte offset of this thread's token row piece (or kOOB)
-  int kpos_b;                    // K element of this thread's token piece within a step
-  int K;
-};
-
-// Weights of K-step ks from HBM into this wave's LDS slot: 8 fully
-// coalesced instructions of 8 rows x 128 bytes.  Lane l of instruction i
-// loads row (i%4)*8 + l/8 of block i/4 and lands in LDS chunk l%8, which
-// therefore holds the row's 16-byte chunk (l%8) ^ (l/8) (XOR swizzle).
-// Chunks past K read zeros.
-template <typename T, int NB>
-__device__ __forceinline__ void load_w(char *slot_wave, const TileState<NB> &st, int ks) {
-  constexpr int KC = 128 / sizeof(T);
-  const bool ok = ks * KC + st.wkpos < st.K;
-  const uint32_t o = ks * 128 + st.wchunk;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int a = i >> 2;
-#if defined(__HIP_DEVICE_COMPILE__)  // the direct-to-LDS load exists only for the device
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        st.ra[a], (lds_void *)(slot_wave + (a * 32 + (i & 3) * 8) * 128), 16,
-        ok ? st.wrow[a][i & 3] + o : kOOB, 0, 0, 0);
-#else
-    (void)a;
-    (void)o;
-    (void)ok;
-#endif
-  }
-}
-
-// Token rows of K-step ks into registers; rows past the chunk and pieces
-// past K read zeros.
-template <typename T, int NB>
-__device__ __forceinline__ void load_b(uint4 (&xr)[NB], const TileState<NB> &st, int ks) {
-  constexpr int KC = 128 / sizeof(T);
-  const bool ok = ks * KC + st.kpos_b < st.K;
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-    xr[i] = bload(st.rb, (ok && st.vob[i] != kOOB) ? st.vob[i] + ks * 128 : kOOB);
-}
-
-// Token piece bp of tile row brow + 32 i lands in chunk bp ^ (brow & 7) of
-// that row (the row's low 3 bits are brow's: 32 i is a multiple of 8).
-template <int NB>
-__device__ __forceinline__ void store_b(char *tile, const uint4 (&xr)[NB], int brow, int bp) {
-  const int chunk = (bp ^ (brow & 7)) * 16;
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-    *reinterpret_cast<uint4 *>(tile + (brow + 32 * i) * kPitch + chunk) = xr[i];
-}
-
-// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
-// memory operations are outstanding, leaving the other counters alone.
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-// MFMAs of one K-step: per 16-byte piece q, 2 x NBR independent MFMAs
-// (consecutive MFMAs never share an accumulator) over the wave's two weight
-// fragments and the NBR live token fragments.
-// NBR is a compile-time count (the tile is dispatched on it once), so the
-// step is straight-line code the compiler can software-pipeline.
-//
-// The slot was filled by the direct-to-LDS loads of two steps ago.  Each
-// such load writes 64 lanes x 16 bytes, but the compiler's dependence
-// tracking sees only the 16 bytes at its base address, so it would let some
-// slot reads pass the fill.  The wait is therefore explicit: every step
-// (and each of the two prologue groups) issues NBR token loads and 8 weight
-// loads, and compiler-level barriers keep the groups in order, so at most
-// 2 * (NBR + 8) younger operations may remain outstanding.  The empty asm
-// keeps the slot reads below the wait.
 // Fragments of 16-byte piece q: the wave's two weight fragments (swizzled
 // slot) and the NBR token fragments (swizzled tile); both operands hold
 // logical chunk h*4 + q of a row whose low 3 bits are r's.
@@ -227,6 +86,20 @@ __device__ __forceinline__ void load_frags(uint4 (&A)[2], uint4 (&B)[NBR], const
     B[nb] = *reinterpret_cast<const uint4 *>(tb + nb * 32 * kPitch + chunk);
 }
 
+// MFMAs of one K-step: per 16-byte piece q, 2 x NBR independent MFMAs
+// (consecutive MFMAs never share an accumulator) over the wave's two weight
+// fragments and the NBR live token fragments.
+// NBR is a compile-time count (the tile is dispatched on it once), so the
+// step is straight-line code the compiler can software-pipeline.
+//
+// The slot was filled by the direct-to-LDS loads of two steps ago.  Each
+// such load writes 64 lanes x 16 bytes, but the compiler's dependence
+// tracking sees only the 16 bytes at its base address, so it would let some
+// slot reads pass the fill.  The wait is therefore explicit: every step
+// (and each of the two prologue groups) issues NBR token loads and 8 weight
+// loads, and compiler-level barriers keep the groups in order, so at most
+// 2 * (NBR + 8) younger operations may remain outstanding.  The empty asm
+// keeps the slot reads below the wait.
 template <typename T, int NBR>
 __device__ __forceinline__ void compute(floatx16 (&acc)[2][NBR], const char *slot_wave,
                                         const char *tile, int r, int h) {
@@ -250,21 +123,6 @@ __device__ __forceinline__ void compute(floatx16 (&acc)[2][NBR], const char *slo
   }
 }
 
-// Workgroup barrier for the token tile.  The tile is written with ordinary
-// LDS stores, so waiting for the LDS counter suffices; the weight slots are
-// private to each wave and their direct-to-LDS loads stay in flight across
-// the barrier (a full fence would wait for them).  The empty asm statements
-// keep the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void tile_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int NB>
-using TileBuf = char[NB * 32 * kPitch];
-
 // One K-step (S = ks mod 6 selects the weight slot ks mod 3 and the token
 // buffer ks mod 2 at compile time): token rows of step ks + 2 are issued
 // before the weights of step ks + 2 (so waiting for them never waits for the
@@ -283,14 +141,6 @@ __device__ __forceinline__ void kstep(int ks, floatx16 (&acc)[2][NBR], char *w0,
   store_b<NBR>(tile[(ks + 1) & 1], xr[(S + 1) & 1], brow, bp);
   tile_barrier();
 }
-
-// Where a tile sits: expert e, weight row block rb, token rows
-// [m0, m0 + mcount), and the K range [k0, k0 + klen) it reduces over (all of
-// K except for a split router GEMM, whose slice s writes partial logits).
-struct TileLoc {
-  int e, rb, m0, mcount;
-  int k0, klen, s;
-};
 
 // The whole K loop and epilogue of one tile with NBR live 32-token blocks
 // (NBR <= NB; the LDS buffers are sized for NB).
@@ -498,11 +348,8 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
   } else {
     ntiles = g.meta[0] * g.nrb;
   }
-  const int quota = (ntiles + 7) / 8;
-  const int loc = blockIdx.x / 8;
-  if (loc >= quota) return;
-  const int v = (blockIdx.x % 8) * quota + loc;
-  if (v >= ntiles) return;
+  const int v = xcd_tile(ntiles);
+  if (v < 0) return;
 
   TileLoc t;
   t.e = 0;
@@ -521,23 +368,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
     t.k0 = t.s * g.kslice;
     t.klen = min(g.kslice, g.K - t.k0);
   } else {
-    // expert of chunk c: the last e with chunk_off[e] <= c (a uniform
-    // binary search over the small prefix table, read through the caches)
-    const int c = v / g.nrb;
-    const int32_t *co = g.chunk_off;
-    int lo = 0, hi = g.N - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (co[mid] <= c) lo = mid;
-      else hi = mid - 1;
-    }
-    t.e = lo;
-    const int local = v - g.nrb * co[t.e];
-    const int nch = co[t.e + 1] - co[t.e];
-    t.rb = local / nch;
-    const int ch = local - t.rb * nch;
-    t.m0 = g.offs[t.e] + ch * MT;
-    t.mcount = min(MT, g.offs[t.e + 1] - t.m0);
+    t = locate_expert_tile(g, v, MT);
   }
   const int nb_rt = (t.mcount + 31) / 32;
   dispatch_tile<T, MODE, NB>(g, t, nb_rt, s_w0, s_w1, s_w2, s_tile);

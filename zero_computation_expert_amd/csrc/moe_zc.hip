@@ -45,7 +45,9 @@ static bool dims_ok(const moe_zc_dims *dm, int *status) {
 }
 
 // Workspace layout; returns the total size.  With base == nullptr only sizes.
-static size_t layout(const moe_zc_dims *dm, char *base, Plan *p) {
+// fp8: E4M3 x (and its exponents) and E4M3 H (and its exponents) instead of
+// an H in the dims' dtype; Y is bfloat16 either way.
+static size_t layout(const moe_zc_dims *dm, char *base, Plan *p, bool fp8 = false) {
   const int64_t T = dm->T;
   const int E = dm->N + dm->Z;
   const int64_t nblk = (T + kTokPerBlk - 1) / kTokPerBlk;
@@ -67,8 +69,13 @@ static size_t layout(const moe_zc_dims *dm, char *base, Plan *p) {
   char *gate = take(static_cast<size_t>(T) * dm->k * 4);
   char *rowmap = take(static_cast<size_t>(T) * dm->k * 4);
   char *tok = take(static_cast<size_t>(pmax) * 4);
-  char *h = take(static_cast<size_t>(pmax) * (dm->N > 0 ? dm->I : 0) * es);
+  const int I = dm->N > 0 ? dm->I : 0;
+  char *h = take(static_cast<size_t>(pmax) * I * (fp8 ? 1 : es));
   char *y = take(static_cast<size_t>(pmax) * dm->d * es);
+  char *qx = fp8 ? take(static_cast<size_t>(T) * dm->d) : nullptr;
+  char *sx = fp8 ? take(static_cast<size_t>(T) * (dm->d / 128)) : nullptr;
+  char *sh = fp8 ? take(static_cast<size_t>(pmax) * (I / 128)) : nullptr;
+  char *sxp = fp8 ? take(static_cast<size_t>(pmax) * (dm->d / 128)) : nullptr;
   if (p) {
     p->logits = reinterpret_cast<float *>(logits);
     p->blockhist = reinterpret_cast<int32_t *>(blockhist);
@@ -81,6 +88,10 @@ static size_t layout(const moe_zc_dims *dm, char *base, Plan *p) {
     p->tok = reinterpret_cast<int32_t *>(tok);
     p->h = h;
     p->y = y;
+    p->qx = qx;
+    p->sx = reinterpret_cast<uint8_t *>(sx);
+    p->sh = reinterpret_cast<uint8_t *>(sh);
+    p->sxp = reinterpret_cast<uint8_t *>(sxp);
   }
   return off;
 }
@@ -104,13 +115,36 @@ struct moe_zc_timer {
 
 using namespace moezc;
 
+// Exponent arrays of FP8 expert weights (nullptr: the bf16 / fp32 path).
+struct Fp8Scales {
+  const uint8_t *gate, *up, *down;
+};
+
+static bool fp8_dims_ok(const moe_zc_dims *dm, int *status) {
+  if (!dims_ok(dm, status)) return false;
+  if (dm->dtype != MOE_ZC_BF16) {
+    *status = MOE_ZC_EDTYPE;
+    return false;
+  }
+  if (dm->d % 128 != 0 || (dm->N > 0 && dm->I % 128 != 0)) {
+    *status = MOE_ZC_EALIGN;
+    return false;
+  }
+  if (dm->d / 128 > kMaxKb8 || (dm->N > 0 && dm->I / 128 > kMaxKb8)) {
+    *status = MOE_ZC_EINVAL;
+    return false;
+  }
+  return true;
+}
+
 static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_router,
                         const float *bias, const void *w_gate, const void *w_up,
                         const void *w_down, void *out, int32_t *counts, int32_t *topk_idx,
                         float *topk_gate, void *workspace, size_t workspace_bytes, void *stream,
-                        moe_zc_timer *timer) {
+                        moe_zc_timer *timer, const Fp8Scales *f8 = nullptr) {
   int st;
-  if (!dims_ok(dm, &st)) return st;
+  if (!(f8 ? fp8_dims_ok(dm, &st) : dims_ok(dm, &st))) return st;
+  if (f8 && dm->T > 0 && dm->N > 0 && (!f8->gate || !f8->up || !f8->down)) return MOE_ZC_EINVAL;
   const int64_t T = dm->T;
   const size_t es = dm->dtype == MOE_ZC_BF16 ? 2 : 4;
   const size_t xbytes = static_cast<size_t>(T) * dm->d * es;
@@ -126,7 +160,7 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   const void *p4[] = {bias, counts, topk_idx, topk_gate};
   for (const void *ptr : p4)
     if (ptr && !aligned(ptr, 4)) return MOE_ZC_EALIGN;
-  const size_t need = layout(dm, nullptr, nullptr);
+  const size_t need = layout(dm, nullptr, nullptr, f8 != nullptr);
   if (T > 0) {
     if (workspace == nullptr || workspace_bytes < need) return MOE_ZC_ENOSPC;
     if (!aligned(workspace, 256)) return MOE_ZC_EALIGN;
@@ -149,8 +183,16 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   // once (a second chunk streams them again); 128 in between; 32 when they
   // receive few (decode-shaped: weight streaming with few rows per expert
   // wants occupancy, not tall tiles).
+  // The FP8 kernels hold twice the bytes per fragment, so their tallest
+  // chunk is 160 rows.
   const int64_t avg_rows = dm->N > 0 ? p.pmax / dm->N : 0;
-  p.nbmax = avg_rows >= 96 ? 8 : (avg_rows >= 24 ? 4 : 1);
+  p.nbmax = avg_rows >= 96 ? (f8 ? 5 : 8) : (avg_rows >= 24 ? 4 : 1);
+  p.fp8 = f8 != nullptr;
+  if (f8) {
+    p.s_gate = f8->gate;
+    p.s_up = f8->up;
+    p.s_down = f8->down;
+  }
   p.rs = router_split(T, p.d, p.E, p.dtype);
   p.x = x;
   p.w_router = w_router;
@@ -160,7 +202,7 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   p.bias = bias;
   p.out = out;
   p.counts = counts;
-  layout(dm, static_cast<char *>(workspace), &p);
+  layout(dm, static_cast<char *>(workspace), &p, f8 != nullptr);
   if (topk_idx) p.idx = topk_idx;
   if (topk_gate) p.gate = topk_gate;
 
@@ -185,11 +227,21 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   const Launch stages[MOE_ZC_NSTAGES] = {launch_router_gemm, launch_topk, launch_scan,
                                          launch_permute,     launch_gate_up, launch_down,
                                          launch_combine};
+  // the FP8 path quantizes x after the permutation (same timer stage) and
+  // runs the FP8 expert GEMMs
+  const Launch stages8[MOE_ZC_NSTAGES] = {
+      launch_router_gemm, launch_topk, launch_scan,
+      [](const Plan &q, hipStream_t ss) {
+        const hipError_t e = launch_permute(q, ss);
+        return (e != hipSuccess || q.N == 0) ? e : launch_quant_x(q, ss);
+      },
+      launch_gate_up8, launch_down8, launch_combine};
+  const Launch *run = p.fp8 ? stages8 : stages;
   if (!mark(0)) return MOE_ZC_EHIP;
   for (int i = 0; i < MOE_ZC_NSTAGES; ++i) {
     const bool ffn = i == MOE_ZC_STAGE_GATE_UP || i == MOE_ZC_STAGE_DOWN;
     if (!(ffn && p.N == 0))
-      if (stages[i](p, s) != hipSuccess) return MOE_ZC_EHIP;
+      if (run[i](p, s) != hipSuccess) return MOE_ZC_EHIP;
     if (!mark(i + 1)) return MOE_ZC_EHIP;
   }
   if (timer) timer->ncalls++;
@@ -197,6 +249,23 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
 }
 
 extern "C" {
+
+size_t moe_zc_workspace_bytes_fp8(const moe_zc_dims *dims) {
+  int st;
+  if (!fp8_dims_ok(dims, &st)) return 0;
+  return layout(dims, nullptr, nullptr, true);
+}
+
+int moe_zc_forward_fp8(const moe_zc_dims *dims, const void *x, const void *W_router,
+                       const float *bias, const uint8_t *W_gate, const uint8_t *W_gate_exp,
+                       const uint8_t *W_up, const uint8_t *W_up_exp, const uint8_t *W_down,
+                       const uint8_t *W_down_exp, void *out, int32_t *counts, int32_t *topk_idx,
+                       float *topk_gate, void *workspace, size_t workspace_bytes, void *stream,
+                       moe_zc_timer *timer) {
+  const Fp8Scales f8 = {W_gate_exp, W_up_exp, W_down_exp};
+  return forward_impl(dims, x, W_router, bias, W_gate, W_up, W_down, out, counts, topk_idx,
+                      topk_gate, workspace, workspace_bytes, stream, timer, &f8);
+}
 
 size_t moe_zc_workspace_bytes(const moe_zc_dims *dims) {
   int st;

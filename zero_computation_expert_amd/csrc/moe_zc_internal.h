@@ -15,6 +15,7 @@ constexpr int kWave = 64;
 constexpr int kTokPerBlk = 16;  // tokens per top-k / permutation block (one wave each in top-k)
 constexpr int kMaxE = 2048;     // experts the top-k kernel holds in registers
 constexpr int kMaxK = 64;       // slots per token (one lane per slot)
+constexpr int kMaxKb8 = 96;    // FP8 path: 128-wide K blocks per row (d, I <= 12288)
 
 // bfloat16 is carried as its 16-bit pattern.
 typedef uint16_t bf16_t;
@@ -128,6 +129,9 @@ hipError_t launch_gate_up(const Plan &p, hipStream_t s);
 hipError_t launch_down(const Plan &p, hipStream_t s);
 hipError_t launch_combine(const Plan &p, hipStream_t s);
 hipError_t launch_zero_counts(const Plan &p, hipStream_t s);
+hipError_t launch_quant_x(const Plan &p, hipStream_t s);
+hipError_t launch_gate_up8(const Plan &p, hipStream_t s);
+hipError_t launch_down8(const Plan &p, hipStream_t s);
 
 // Everything one forward call needs, resolved on the host.
 struct Plan {
@@ -143,6 +147,10 @@ struct Plan {
   const void *x, *w_router, *w_gate, *w_up, *w_down;
   const float *bias;
   void *out;
+  // FP8 experts (moe_zc_forward_fp8): weights are E4M3 bytes, with E8M0
+  // exponents per [128,128] block
+  bool fp8;
+  const uint8_t *s_gate, *s_up, *s_down;
   int32_t *counts;
   int32_t *idx;   // caller's or workspace
   float *gate;    // caller's or workspace
@@ -154,8 +162,12 @@ struct Plan {
   int32_t *meta;        // [0] total chunks, [1] total pairs P
   int32_t *rowmap;      // [T, k] permuted row of slot (t, j), -1 for zero experts
   int32_t *tok;         // [pmax] token of each permuted row
-  void *h;              // [pmax, I] SwiGLU activations
+  void *h;              // [pmax, I] SwiGLU activations (FP8 path: E4M3 bytes)
   void *y;              // [pmax, d] expert outputs
+  void *qx;             // FP8 path: [T, d] E4M3 x
+  uint8_t *sx;          // FP8 path: [T, d/128] exponents of x
+  uint8_t *sxp;         // FP8 path: [pmax, d/128] the same, rows in permuted order
+  uint8_t *sh;          // FP8 path: [pmax, I/128] exponents of H
 };
 
 }  // namespace moezc
