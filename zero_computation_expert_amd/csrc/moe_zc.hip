@@ -178,15 +178,13 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   p.dtype = dm->dtype;
   p.nblk = static_cast<int>((T + kTokPerBlk - 1) / kTokPerBlk);
   p.pmax = T * std::min(dm->k, dm->N);
-  // Chunk height of the expert GEMMs (32-token blocks): 256 token rows when
-  // experts receive many rows on average, so that an expert's weights stream
-  // once (a second chunk streams them again); 128 in between; 32 when they
-  // receive few (decode-shaped: weight streaming with few rows per expert
-  // wants occupancy, not tall tiles).
-  // The FP8 kernels hold twice the bytes per fragment, so their tallest
-  // chunk is 160 rows.
+  // Chunk height of the expert GEMMs (32-token blocks): 160 token rows (the
+  // tallest chunk whose three token tiles fit in LDS beside the weight
+  // slots) when experts receive many rows on average, 128 in between, 32
+  // when they receive few (decode-shaped: weight streaming with few rows
+  // per expert wants occupancy, not tall tiles).
   const int64_t avg_rows = dm->N > 0 ? p.pmax / dm->N : 0;
-  p.nbmax = avg_rows >= 96 ? (f8 ? 5 : 8) : (avg_rows >= 24 ? 4 : 1);
+  p.nbmax = avg_rows >= 96 ? 5 : (avg_rows >= 24 ? 4 : 1);
   p.fp8 = f8 != nullptr;
   if (f8) {
     p.s_gate = f8->gate;

@@ -141,7 +141,7 @@ struct Plan {
   int dtype;  // moe_zc_dtype
   int nblk;   // ceil(T / kTokPerBlk)
   int64_t pmax;  // T * min(k, N): upper bound of (token, FFN expert) pairs
-  int nbmax;  // 32-token column blocks per GEMM chunk (1, 4 or 8)
+  int nbmax;  // 32-token column blocks per GEMM chunk (1, 4 or 5)
   RouterSplit rs;  // router GEMM partition
   // caller tensors
   const void *x, *w_router, *w_gate, *w_up, *w_down;
