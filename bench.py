@@ -79,12 +79,21 @@ def cpu_model():
 # with the hash of the kernel source it was measured on; a summary taken on
 # another version of the kernel is not reported.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_prod_hbm_traffic.txt")
-KERNEL_SRC = os.path.join(ROOT, "zero_computation_expert_amd", "csrc", "gemm.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "zero_computation_expert_amd", "csrc", f)
+               for f in ("gemm.hip", "gemm_common.h")]
+
+
+def kernel_source_hash():
+    """sha256 over the bf16 GEMM kernel's sources (gemm.hip, gemm_common.h)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload):
-    import hashlib
-
     if workload != "prod" or not os.path.exists(TRAFFIC_FILE):
         return None
     fields = {}
@@ -92,8 +101,7 @@ def measured_traffic(workload):
         if ":" in line and not line.startswith(" "):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if fields.get("kernel_source_sha256") != src_hash:
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
