@@ -78,30 +78,32 @@ def cpu_model():
 # and WRITE_SIZE in their own runs and kept in a committed summary together
 # with the hash of the kernel source it was measured on; a summary taken on
 # another version of the kernel is not reported.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_prod_hbm_traffic.txt")
-KERNEL_SRCS = [os.path.join(ROOT, "zero_computation_expert_amd", "csrc", f)
-               for f in ("gemm.hip", "gemm_common.h")]
+def traffic_file(workload, fp8):
+    kind = "gemm8" if fp8 else "gemm"
+    return os.path.join(ROOT, "profiles", f"{kind}_gate_up_{workload}_hbm_traffic.txt")
 
 
-def kernel_source_hash():
-    """sha256 over the bf16 GEMM kernel's sources (gemm.hip, gemm_common.h)."""
+def kernel_source_hash(fp8=False):
+    """sha256 over the gate/up GEMM kernel's sources (gemm.hip or gemm_fp8.hip,
+    and gemm_common.h)."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in KERNEL_SRCS:
-        h.update(open(f, "rb").read())
+    for f in ("gemm_fp8.hip" if fp8 else "gemm.hip", "gemm_common.h"):
+        h.update(open(os.path.join(ROOT, "zero_computation_expert_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    if workload != "prod" or not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(workload, fp8=False):
+    path = traffic_file(workload, fp8)
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith(" "):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_hash():
+    if fields.get("kernel_source_sha256") != kernel_source_hash(fp8):
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
@@ -231,7 +233,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                "traffic": None if args.fp8 else measured_traffic(cfg.name),
+                "traffic": measured_traffic(cfg.name, args.fp8),
                 "algorithmic_bytes_per_launch": alg["gate_up"]["bytes"],
                 "avg_launch_ms": round(stage_avg["gate_up"], 4)}
     kernels = {}
