@@ -73,6 +73,11 @@ def _load():
                                                          vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_forward_fp8.argtypes = [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                            vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_token_backward.argtypes = [i32, i32, i32, i32, i32, vp, i32] + [vp] * 13
+        lib.oracle_backward.argtypes = [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_expert_wgrad_row.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, i32,
+                                                vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -292,3 +297,91 @@ def forward_fp8(x, w_router, bias, qwg, swg, qwu, swu, qwd, swd, N: int, Z: int,
                                _ptr(qwg), _ptr(swg), _ptr(qwu), _ptr(swu), _ptr(qwd), _ptr(swd),
                                _ptr(out), _ptr(cnt), _ptr(idx), _ptr(gate), _ptr(margin))
     return {"out": out, "counts": cnt, "idx": idx, "gate": gate, "margin": margin}
+
+
+def token_backward(x_row, dt: str, w_router, N: int, idx_row, gate_row, dout_row,
+                   experts: dict) -> dict:
+    """Backward of one token with given routing: dict(dx [d], dgate [k],
+    dl [E] (router-logit gradient), h/dg/du [k, I] (rows of FFN slots)).
+    ``experts[e] = (W_gate[e], W_up[e], W_down[e])`` for every FFN expert in
+    ``idx_row``."""
+    x_row = _storage(x_row, dt)
+    w_router = _storage(w_router, dt)
+    d = x_row.shape[0]
+    E = w_router.shape[0]
+    idx_row = _c(idx_row, np.int32)
+    gate_row = _c(gate_row, np.float32)
+    dout_row = _c(dout_row, np.float32)
+    k = idx_row.shape[0]
+    keep = []
+    pg = (ctypes.c_void_p * k)()
+    pu = (ctypes.c_void_p * k)()
+    pd = (ctypes.c_void_p * k)()
+    I = 1
+    for j in range(k):
+        e = int(idx_row[j])
+        if e < N:
+            g, u, dn = (_storage(a, dt) for a in experts[e])
+            keep += [g, u, dn]
+            I = g.shape[0]
+            pg[j], pu[j], pd[j] = g.ctypes.data, u.ctypes.data, dn.ctypes.data
+    dx = np.empty(d, dtype=np.float32)
+    dgate = np.empty(k, dtype=np.float32)
+    dl = np.empty(E, dtype=np.float32)
+    h, dg, du = (np.zeros((k, I), dtype=np.float32) for _ in range(3))
+    _load().oracle_token_backward(d, I, N, E, k, _ptr(x_row), _DT[dt], _ptr(w_router),
+                                  _ptr(idx_row), _ptr(gate_row), _ptr(dout_row), pg, pu, pd,
+                                  _ptr(dx), _ptr(dgate), _ptr(dl), _ptr(h), _ptr(dg), _ptr(du))
+    return {"dx": dx, "dgate": dgate, "dl": dl, "h": h, "dg": dg, "du": du}
+
+
+def backward(x, w_router, w_gate, w_up, w_down, idx, gate, dout, N: int, Z: int, dt: str,
+             grads=None) -> dict:
+    """Whole backward with given routing.  Returns dict(dx, dw_router, dw_gate,
+    dw_up, dw_down); the weight gradients are accumulated into ``grads``
+    (a dict of fp32 arrays with those keys) when given, else into zeros."""
+    x = _storage(x, dt)
+    w_router = _storage(w_router, dt)
+    T, d = x.shape
+    E = N + Z
+    idx = _c(idx, np.int32)
+    gate = _c(gate, np.float32)
+    dout = _c(dout, np.float32)
+    k = idx.shape[1]
+    if N > 0:
+        w_gate, w_up, w_down = (_storage(a, dt) for a in (w_gate, w_up, w_down))
+        I = w_gate.shape[1]
+    else:
+        w_gate = w_up = w_down = None
+        I = 1
+    if grads is None:
+        grads = {"dw_router": np.zeros((E, d), np.float32),
+                 "dw_gate": np.zeros((max(N, 0), I, d), np.float32),
+                 "dw_up": np.zeros((max(N, 0), I, d), np.float32),
+                 "dw_down": np.zeros((max(N, 0), d, I), np.float32)}
+    g = {key: _c(grads[key], np.float32) for key in ("dw_router", "dw_gate", "dw_up", "dw_down")}
+    dx = np.empty((T, d), dtype=np.float32)
+    _load().oracle_backward(T, d, I, N, Z, k, _DT[dt], _ptr(x), _ptr(w_router), _ptr(w_gate),
+                            _ptr(w_up), _ptr(w_down), _ptr(idx), _ptr(gate), _ptr(dout), _ptr(dx),
+                            _ptr(g["dw_router"]), _ptr(g["dw_gate"]), _ptr(g["dw_up"]),
+                            _ptr(g["dw_down"]))
+    out = {"dx": dx}
+    out.update(g)
+    return out
+
+
+def expert_wgrad_row(x_rows, dt: str, dout_rows, gates, wg, wu, wd, r: int) -> dict:
+    """Row r of dW_gate[e] and dW_up[e] and column r of dW_down[e] from the n
+    tokens routed to expert e (x_rows [n, d] in storage dtype, dout_rows
+    [n, d] fp32, gates [n], tokens in ascending order)."""
+    x_rows = _storage(x_rows, dt)
+    n, d = x_rows.shape
+    wg, wu, wd = (_storage(a, dt) for a in (wg, wu, wd))
+    I = wg.shape[0]
+    dout_rows = _c(dout_rows, np.float32)
+    gates = _c(gates, np.float32)
+    dwg, dwu, dwd = (np.empty(d, dtype=np.float32) for _ in range(3))
+    _load().oracle_expert_wgrad_row(d, I, n, _ptr(x_rows), _DT[dt], _ptr(dout_rows), _ptr(gates),
+                                    _ptr(wg), _ptr(wu), _ptr(wd), r, _ptr(dwg), _ptr(dwu),
+                                    _ptr(dwd))
+    return {"dw_gate_row": dwg, "dw_up_row": dwu, "dw_down_col": dwd}

@@ -486,3 +486,212 @@ void oracle_forward_fp8(int64_t T, int d, int I, int N, int Z, int k, int dt, co
                                    out);
   free(logits);
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of the block (training).
+ * [LCF] section 5 "training infrastructure": the backward's grouped GEMMs,
+ * the weight-gradient GEMMs with the fp32 accumulation fused into them
+ * ("GemmAdd") and a deterministic scatter-add for gradient aggregation.
+ * The pages give the kernels, not the formulas; the formulas are the chain
+ * rule applied to the forward above, with the routing held fixed (the
+ * top-k selection and the bias are not differentiated; the bias moves only
+ * through the controller):
+ *   zero slot j:  dgate_j = <dout, x>;                dx += gate_j dout
+ *   FFN slot j, expert e (g = Wg x, u = Wu x, s = sigmoid(g), h = g s u):
+ *     v = Wd^T dout;  dgate_j = <v, h>;  dh = gate_j v;
+ *     dg = dh u s (1 + g (1 - s));  du = dh g s;
+ *     dx += Wg^T dg + Wu^T du;
+ *     dWd[e] += (gate_j dout) h^T;  dWg[e] += dg x^T;  dWu[e] += du x^T
+ *   router (p = softmax(l), gate_j = p[idx_j]):
+ *     dp[e] = dgate_j where idx_j = e, else 0;
+ *     dl = p * (dp - <p, dp>);  dx += Wr^T dl;  dWr += dl x^T
+ * Weight gradients are accumulated into the caller's fp32 arrays.  Every sum
+ * runs in ascending index order; weight gradients add tokens in ascending
+ * order.
+ * ------------------------------------------------------------------------ */
+
+/* One token: dx (d floats), dgate (k), dl (E: gradient of the router
+ * logits); per-slot h, dg, du ([k, I] each, rows of zero slots untouched).
+ * wg/wu/wd[j]: the matrices of the expert in slot j (unused for zero slots). */
+void oracle_token_backward(int d, int I, int N, int E, int k, const void *x_row, int dt,
+                           const void *w_router, const int32_t *idx, const float *gate,
+                           const float *dout, const void *const *wg, const void *const *wu,
+                           const void *const *wd, float *dx, float *dgate, float *dl,
+                           float *h_s, float *dg_s, float *du_s) {
+  float *x = (float *)malloc(sizeof(float) * (size_t)d);
+  float *l = (float *)malloc(sizeof(float) * (size_t)E);
+  float *p = (float *)malloc(sizeof(float) * (size_t)E);
+  float *dp = (float *)malloc(sizeof(float) * (size_t)E);
+  for (int c = 0; c < d; ++c) x[c] = orc_ld(x_row, c, dt);
+  /* forward quantities: logits and probabilities of this token */
+  for (int e = 0; e < E; ++e) {
+    float acc = 0.0f;
+    for (int c = 0; c < d; ++c) acc += x[c] * orc_ld(w_router, (int64_t)e * d + c, dt);
+    l[e] = acc;
+  }
+  orc_softmax(E, l, p);
+  float zsum = 0.0f;
+  for (int j = 0; j < k; ++j)
+    if (idx[j] >= N) zsum += gate[j];
+  for (int c = 0; c < d; ++c) dx[c] = zsum * dout[c];
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[j];
+    if (e >= N) {
+      float acc = 0.0f;
+      for (int c = 0; c < d; ++c) acc += dout[c] * x[c];
+      dgate[j] = acc;
+      continue;
+    }
+    float *h = h_s + (int64_t)j * I, *dg = dg_s + (int64_t)j * I, *du = du_s + (int64_t)j * I;
+    float dgj = 0.0f;
+    for (int r = 0; r < I; ++r) {
+      float g = 0.0f, u = 0.0f, vr = 0.0f;
+      for (int c = 0; c < d; ++c) {
+        g += orc_ld(wg[j], (int64_t)r * d + c, dt) * x[c];
+        u += orc_ld(wu[j], (int64_t)r * d + c, dt) * x[c];
+      }
+      for (int c = 0; c < d; ++c) vr += orc_ld(wd[j], (int64_t)c * I + r, dt) * dout[c];
+      const float s = 1.0f / (1.0f + expf(-g));
+      h[r] = g * s * u;
+      dgj += vr * h[r];
+      const float dh = gate[j] * vr;
+      dg[r] = dh * u * s * (1.0f + g * (1.0f - s));
+      du[r] = dh * g * s;
+    }
+    dgate[j] = dgj;
+    for (int c = 0; c < d; ++c) {
+      float acc = dx[c];
+      for (int r = 0; r < I; ++r) acc += orc_ld(wg[j], (int64_t)r * d + c, dt) * dg[r];
+      for (int r = 0; r < I; ++r) acc += orc_ld(wu[j], (int64_t)r * d + c, dt) * du[r];
+      dx[c] = acc;
+    }
+  }
+  /* router: softmax backward through the selected gates */
+  for (int e = 0; e < E; ++e) dp[e] = 0.0f;
+  for (int j = 0; j < k; ++j) dp[idx[j]] = dgate[j];
+  float pdp = 0.0f;
+  for (int e = 0; e < E; ++e) pdp += p[e] * dp[e];
+  for (int e = 0; e < E; ++e) dl[e] = p[e] * (dp[e] - pdp);
+  for (int c = 0; c < d; ++c) {
+    float acc = 0.0f;
+    for (int e = 0; e < E; ++e) acc += orc_ld(w_router, (int64_t)e * d + c, dt) * dl[e];
+    dx[c] += acc;
+  }
+  free(x);
+  free(l);
+  free(p);
+  free(dp);
+}
+
+/* The whole backward for tokens [0, T) with given routing (idx, gate from
+ * the forward) and output gradient dout [T, d] (fp32).  dx [T, d] is
+ * overwritten; dw_router [E, d], dw_gate / dw_up [N, I, d] and dw_down
+ * [N, d, I] (fp32) are accumulated into. */
+void oracle_backward(int64_t T, int d, int I, int N, int Z, int k, int dt, const void *x,
+                     const void *w_router, const void *w_gate, const void *w_up,
+                     const void *w_down, const int32_t *idx, const float *gate,
+                     const float *dout, float *dx, float *dw_router, float *dw_gate,
+                     float *dw_up, float *dw_down) {
+  const int E = N + Z;
+  const size_t es = dt == ORC_F32 ? 4 : 2;
+  const size_t per = (size_t)I * (size_t)d * es;
+  const size_t Ts = (size_t)(T > 0 ? T : 1), Is = (size_t)(I > 0 ? I : 1);
+  float *dl = (float *)malloc(sizeof(float) * Ts * (size_t)E);
+  float *dgate = (float *)malloc(sizeof(float) * Ts * (size_t)k);
+  float *h = (float *)malloc(sizeof(float) * Ts * (size_t)k * Is);
+  float *dg = (float *)malloc(sizeof(float) * Ts * (size_t)k * Is);
+  float *du = (float *)malloc(sizeof(float) * Ts * (size_t)k * Is);
+#pragma omp parallel
+  {
+    const void **pg = (const void **)malloc(sizeof(void *) * (size_t)k);
+    const void **pu = (const void **)malloc(sizeof(void *) * (size_t)k);
+    const void **pd = (const void **)malloc(sizeof(void *) * (size_t)k);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[t * k + j];
+        const int ffn = e < N;
+        pg[j] = ffn ? (const char *)w_gate + (size_t)e * per : NULL;
+        pu[j] = ffn ? (const char *)w_up + (size_t)e * per : NULL;
+        pd[j] = ffn ? (const char *)w_down + (size_t)e * per : NULL;
+      }
+      const size_t so = (size_t)t * (size_t)k * Is;
+      oracle_token_backward(d, I, N, E, k, (const char *)x + (size_t)t * (size_t)d * es, dt,
+                            w_router, idx + t * k, gate + t * k, dout + t * (int64_t)d, pg, pu,
+                            pd, dx + t * (int64_t)d, dgate + t * k, dl + t * (int64_t)E, h + so,
+                            dg + so, du + so);
+    }
+    free(pg);
+    free(pu);
+    free(pd);
+  }
+  /* expert weight gradients, one expert at a time, tokens ascending */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int e = 0; e < N; ++e) {
+    float *gwg = dw_gate + (int64_t)e * I * d, *gwu = dw_up + (int64_t)e * I * d;
+    float *gwd = dw_down + (int64_t)e * d * I;
+    for (int64_t t = 0; t < T; ++t) {
+      for (int j = 0; j < k; ++j) {
+        if (idx[t * k + j] != e) continue;
+        const size_t so = ((size_t)t * (size_t)k + (size_t)j) * Is;
+        for (int r = 0; r < I; ++r)
+          for (int c = 0; c < d; ++c) {
+            const float xc = orc_ld(x, t * (int64_t)d + c, dt);
+            gwg[(int64_t)r * d + c] += dg[so + r] * xc;
+            gwu[(int64_t)r * d + c] += du[so + r] * xc;
+          }
+        const float gt = gate[t * k + j];
+        for (int c = 0; c < d; ++c) {
+          const float dy = gt * dout[t * (int64_t)d + c];
+          for (int r = 0; r < I; ++r) gwd[(int64_t)c * I + r] += dy * h[so + r];
+        }
+      }
+    }
+  }
+  /* router weight gradient, tokens ascending */
+#pragma omp parallel for schedule(static)
+  for (int e = 0; e < E; ++e)
+    for (int64_t t = 0; t < T; ++t) {
+      const float g = dl[t * (int64_t)E + e];
+      for (int c = 0; c < d; ++c)
+        dw_router[(int64_t)e * d + c] += g * orc_ld(x, t * (int64_t)d + c, dt);
+    }
+  free(dl);
+  free(dgate);
+  free(h);
+  free(dg);
+  free(du);
+}
+
+/* Rows of one expert's weight gradients from the tokens routed to it (for
+ * sampled checks at sizes where the whole backward is too slow): given the
+ * n routed tokens' x (dtype, [n, d]), dout ([n, d] fp32) and gates, in
+ * ascending token order, the gradient contributions of this call for row r:
+ * dwg_row = dWg[e][r, :], dwu_row = dWu[e][r, :] (d floats each) and
+ * dwd_col = dWd[e][:, r] (d floats), each summed over the n tokens. */
+void oracle_expert_wgrad_row(int d, int I, int n, const void *x_rows, int dt,
+                             const float *dout_rows, const float *gates, const void *wg,
+                             const void *wu, const void *wd, int r, float *dwg_row,
+                             float *dwu_row, float *dwd_col) {
+  for (int c = 0; c < d; ++c) dwg_row[c] = dwu_row[c] = dwd_col[c] = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float g = 0.0f, u = 0.0f, vr = 0.0f;
+    for (int c = 0; c < d; ++c) {
+      const float xc = orc_ld(x_rows, (int64_t)i * d + c, dt);
+      g += orc_ld(wg, (int64_t)r * d + c, dt) * xc;
+      u += orc_ld(wu, (int64_t)r * d + c, dt) * xc;
+    }
+    for (int c = 0; c < d; ++c) vr += orc_ld(wd, (int64_t)c * I + r, dt) * dout_rows[(int64_t)i * d + c];
+    const float s = 1.0f / (1.0f + expf(-g));
+    const float h = g * s * u;
+    const float dh = gates[i] * vr;
+    const float dg = dh * u * s * (1.0f + g * (1.0f - s));
+    const float du = dh * g * s;
+    for (int c = 0; c < d; ++c) {
+      const float xc = orc_ld(x_rows, (int64_t)i * d + c, dt);
+      dwg_row[c] += dg * xc;
+      dwu_row[c] += du * xc;
+      dwd_col[c] += gates[i] * dout_rows[(int64_t)i * d + c] * h;
+    }
+  }
+}

@@ -36,6 +36,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _GOLDEN = os.path.join(os.path.dirname(_HERE), "tests", "golden")
 
 TID_X, TID_WR, TID_BIAS, TID_WG, TID_WU, TID_WD = 0, 1, 2, 3, 4, 5
+TID_DOUT = 6  # output gradient of the backward, N(0, 1) in the inputs' dtype
 
 
 @dataclass(frozen=True)
@@ -165,6 +166,12 @@ def host_x(cfg: Config, t0: int = 0, nt: Optional[int] = None) -> np.ndarray:
     return host_normal((nt, cfg.d), t0 * cfg.d, cfg.seed, TID_X, 1.0, cfg.dtype)
 
 
+def host_dout(cfg: Config, t0: int = 0, nt: Optional[int] = None) -> np.ndarray:
+    """Output gradient rows [t0, t0+nt) for the backward (the inputs' dtype)."""
+    nt = cfg.T - t0 if nt is None else nt
+    return host_normal((nt, cfg.d), t0 * cfg.d, cfg.seed, TID_DOUT, 1.0, cfg.dtype)
+
+
 def host_router(cfg: Config) -> np.ndarray:
     return host_normal((cfg.E, cfg.d), 0, cfg.seed, TID_WR, sigma_weights(cfg), cfg.dtype)
 
@@ -272,3 +279,8 @@ def device_inputs(cfg: Config, device="cuda:0") -> dict:
         shape = (cfg.N, cfg.I, cfg.d) if w != "down" else (cfg.N, cfg.d, cfg.I)
         out["W_" + w] = device_normal(shape, 0, cfg.seed, tid, sw, cfg.dtype, device)
     return out
+
+
+def device_dout(cfg: Config, device="cuda:0"):
+    """The output gradient of host_dout, generated in device memory."""
+    return device_normal((cfg.T, cfg.d), 0, cfg.seed, TID_DOUT, 1.0, cfg.dtype, device)
