@@ -148,7 +148,20 @@ enum {
   MOE_ZC_STAGE_GATE_UP = 4, /* step 3: gate/up GEMM + SwiGLU          */
   MOE_ZC_STAGE_DOWN = 5,    /* step 3: down GEMM                      */
   MOE_ZC_STAGE_COMBINE = 6, /* steps 4-5: zero experts + combine      */
-  MOE_ZC_NSTAGES = 7
+  MOE_ZC_NSTAGES = 7,
+  /* stages of moe_zc_backward */
+  MOE_ZC_BSTAGE_ROUTE = 0,         /* routing bookkeeping, permuted x / dy rows */
+  MOE_ZC_BSTAGE_ROUTER = 1,        /* router logits GEMM (recomputed)           */
+  MOE_ZC_BSTAGE_RECOMPUTE = 2,     /* G = X W_gate^T, U = X W_up^T              */
+  MOE_ZC_BSTAGE_DGRAD_V = 3,       /* W_down^T dout -> dG, dU, H, gate grads    */
+  MOE_ZC_BSTAGE_ROUTER_BWD = 4,    /* softmax backward -> router-logit grads    */
+  MOE_ZC_BSTAGE_WGRAD_DOWN = 5,    /* dW_down += dY^T H                         */
+  MOE_ZC_BSTAGE_WGRAD_GATE_UP = 6, /* dW_gate += dG^T X, dW_up += dU^T X        */
+  MOE_ZC_BSTAGE_DGRAD_X = 7,       /* dG W_gate + dU W_up (permuted rows)       */
+  MOE_ZC_BSTAGE_DX = 8,            /* router part of dx, gather of dx           */
+  MOE_ZC_BSTAGE_WGRAD_ROUTER = 9,  /* dW_router += dl^T x                       */
+  MOE_ZC_BWD_NSTAGES = 10,
+  MOE_ZC_MAX_STAGES = 10
 };
 
 typedef struct moe_zc_timer moe_zc_timer;
@@ -166,13 +179,59 @@ int moe_zc_forward_timed(const moe_zc_dims *dims, const void *x, const void *W_r
                          moe_zc_timer *timer);
 
 /* Waits for the recorded events; writes the number of recorded calls and
- * the per-stage millisecond sums (ms[MOE_ZC_NSTAGES]). */
+ * the per-stage millisecond sums (ms[MOE_ZC_MAX_STAGES]; a forward call adds
+ * to its MOE_ZC_NSTAGES stages, a backward call to its MOE_ZC_BWD_NSTAGES). */
 int moe_zc_timer_read(moe_zc_timer *timer, int *ncalls, float *ms);
 
 /* Forgets the recorded calls. */
 void moe_zc_timer_reset(moe_zc_timer *timer);
 
 void moe_zc_timer_destroy(moe_zc_timer *timer);
+
+/* ------------------------------------------------------------------------
+ * Backward of the block (training).
+ *
+ * LongCat-Flash technical-report summary page, section 5 "training
+ * infrastructure": grouped GEMMs for the backward, fp32 accumulation of the
+ * weight gradients fused into the GEMM ("GemmAdd"), deterministic gradient
+ * aggregation.  The formulas are the chain rule through moe_zc_forward with
+ * the routing held fixed (selection and bias are not differentiated):
+ *   zero slot j:  dgate_j = <dout, x>,  dx += gate_j dout
+ *   FFN slot j, expert e (g = W_gate[e] x, u = W_up[e] x, s = sigmoid(g),
+ *   h = g s u):  v = W_down[e]^T dout,  dgate_j = <v, h>,  dh = gate_j v,
+ *     dg = dh u s (1 + g (1 - s)),  du = dh g s,
+ *     dx += W_gate[e]^T dg + W_up[e]^T du,
+ *     dW_down[e] += gate_j dout h^T,  dW_gate[e] += dg x^T,  dW_up[e] += du x^T
+ *   router (p = softmax(x W_router^T), gate_j = p[idx_j]):
+ *     dl = p * (dp - <p, dp>), dp[idx_j] = dgate_j;
+ *     dx += W_router^T dl,  dW_router += dl x^T
+ *
+ *   dims        as for moe_zc_forward; bfloat16 only (MOE_ZC_EDTYPE
+ *               otherwise); d and I multiples of 8
+ *   x, W_*      the forward's inputs (bfloat16, layouts of moe_zc_forward)
+ *   topk_idx    [T, k] int32, topk_gate [T, k] fp32: the forward's routing
+ *               outputs.  An entry outside [0, N+Z), or repeating an earlier
+ *               expert of its token, is ignored (that slot gets no gradient).
+ *   dout        [T, d] bfloat16, the gradient of the forward's output
+ *   dx          [T, d] bfloat16, overwritten (must not overlap x or dout)
+ *   dW_router   [N+Z, d] fp32, dW_gate / dW_up [N, I, d] fp32,
+ *   dW_down     [N, d, I] fp32: accumulated into (+=); an expert no token
+ *               selects is not touched
+ *   workspace   device memory of moe_zc_backward_workspace_bytes(dims)
+ *               bytes, 256-byte aligned (sized for every slot on an FFN
+ *               expert)
+ *   stream      hipStream_t; timer nullable (stages MOE_ZC_BSTAGE_*)
+ * The result is deterministic: every sum runs in a fixed order, and every
+ * gradient element has one writer.  Returns MOE_ZC_OK or an error status;
+ * on error nothing is enqueued.
+ * ------------------------------------------------------------------------ */
+size_t moe_zc_backward_workspace_bytes(const moe_zc_dims *dims);
+
+int moe_zc_backward(const moe_zc_dims *dims, const void *x, const void *W_router,
+                    const void *W_gate, const void *W_up, const void *W_down,
+                    const int32_t *topk_idx, const float *topk_gate, const void *dout, void *dx,
+                    float *dW_router, float *dW_gate, float *dW_up, float *dW_down,
+                    void *workspace, size_t workspace_bytes, void *stream, moe_zc_timer *timer);
 
 /* ------------------------------------------------------------------------
  * Block-scaled FP8 experts.

@@ -202,3 +202,46 @@ def test_forward_fp8_rejects():
     assert moe.lib().moe_zc_workspace_bytes_fp8(ctypes.byref(D(T=64, d=200, I=128))) == 0
     assert (moe.lib().moe_zc_workspace_bytes_fp8(ctypes.byref(D(T=4096, d=256, I=128)))
             > moe.lib().moe_zc_workspace_bytes_fp8(ctypes.byref(D(T=64, d=256, I=128))))
+
+
+def bwd_call(dims, ws_bytes=None, **kw):
+    lib = moe.lib()
+    if ws_bytes is None:
+        ws_bytes = lib.moe_zc_backward_workspace_bytes(ctypes.byref(dims))
+    p = {"x": A, "wr": 2 * A, "wg": 3 * A, "wu": 4 * A, "wd": 5 * A, "idx": 6 * A,
+         "gate": 7 * A, "dout": 8 * A, "dx": 9 * A, "dwr": 10 * A, "dwg": 11 * A, "dwu": 12 * A,
+         "dwd": 13 * A, "ws": 16 * A}
+    p.update(kw)
+    st = lib.moe_zc_backward(ctypes.byref(dims), p["x"], p["wr"], p["wg"], p["wu"], p["wd"],
+                             p["idx"], p["gate"], p["dout"], p["dx"], p["dwr"], p["dwg"],
+                             p["dwu"], p["dwd"], p["ws"], ws_bytes, None, None)
+    assert st != 0, "a test call passed validation: it would have launched work"
+    return st
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({"x": None}, EINVAL),
+    ({"idx": None}, EINVAL),
+    ({"gate": None}, EINVAL),
+    ({"dout": None}, EINVAL),
+    ({"dx": None}, EINVAL),
+    ({"dwr": None}, EINVAL),
+    ({"dwd": None}, EINVAL),
+    ({"dx": A + 64}, EINVAL),                # dx overlaps x
+    ({"dx": 8 * A + 32}, EINVAL),            # dx overlaps dout
+    ({"dout": 8 * A + 8}, EALIGN),
+    ({"dwg": 11 * A + 2}, EALIGN),
+    ({"ws": None}, ENOSPC),
+    ({"ws": 16 * A + 16}, EALIGN),
+])
+def test_backward_rejects(kw, expect):
+    assert bwd_call(D(), **kw) == expect
+
+
+def test_backward_rejects_dims():
+    assert bwd_call(D(dtype=moe.F32)) == EDTYPE
+    assert bwd_call(D(d=100)) == EALIGN
+    assert bwd_call(D(), ws_bytes=100) == ENOSPC
+    assert moe.lib().moe_zc_backward_workspace_bytes(ctypes.byref(D(dtype=moe.F32))) == 0
+    big = moe.lib().moe_zc_backward_workspace_bytes(ctypes.byref(D(T=4096)))
+    assert big > moe.lib().moe_zc_backward_workspace_bytes(ctypes.byref(D(T=64))) > 0

@@ -19,10 +19,14 @@ F32, BF16 = 0, 1
 STATUS = {0: "MOE_ZC_OK", -1: "MOE_ZC_EINVAL", -2: "MOE_ZC_EDTYPE", -3: "MOE_ZC_EALIGN",
           -4: "MOE_ZC_ENOSPC", -5: "MOE_ZC_EHIP"}
 STAGES = ("router", "topk", "scan", "permute", "gate_up", "down", "combine")
+BWD_STAGES = ("route", "router", "recompute", "dgrad_v", "router_bwd", "wgrad_down",
+              "wgrad_gate_up", "dgrad_x", "dx", "wgrad_router")
+MAX_STAGES = 10
 EXPORTS = ("moe_zc_workspace_bytes", "moe_zc_forward", "moe_zc_status_string",
            "moe_zc_timer_create", "moe_zc_forward_timed", "moe_zc_timer_read",
            "moe_zc_timer_reset", "moe_zc_timer_destroy", "moe_zc_bias_update",
-           "moe_zc_quantize_fp8", "moe_zc_workspace_bytes_fp8", "moe_zc_forward_fp8")
+           "moe_zc_quantize_fp8", "moe_zc_workspace_bytes_fp8", "moe_zc_forward_fp8",
+           "moe_zc_backward_workspace_bytes", "moe_zc_backward")
 
 
 class MoeZcError(RuntimeError):
@@ -75,6 +79,10 @@ def lib():
         L.moe_zc_forward_fp8.restype = ctypes.c_int
         L.moe_zc_forward_fp8.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, vp, sz, vp, vp]
+        L.moe_zc_backward_workspace_bytes.restype = sz
+        L.moe_zc_backward_workspace_bytes.argtypes = [dims_p]
+        L.moe_zc_backward.restype = ctypes.c_int
+        L.moe_zc_backward.argtypes = [dims_p] + [vp] * 14 + [sz, vp, vp]
         f32 = ctypes.c_float
         L.moe_zc_bias_update.restype = ctypes.c_int
         L.moe_zc_bias_update.argtypes = [ctypes.c_int32, ctypes.c_int64, vp, vp, vp, vp, f32, f32,
@@ -118,19 +126,21 @@ def _ptr(t) -> Optional[int]:
 
 
 class Timer:
-    """Per-stage HIP-event timer over up to ``max_calls`` forward calls."""
+    """Per-stage HIP-event timer over up to ``max_calls`` forward (or, with
+    ``stages=BWD_STAGES``, backward) calls."""
 
-    def __init__(self, max_calls: int):
+    def __init__(self, max_calls: int, stages=STAGES):
         h = ctypes.c_void_p()
         _check(lib().moe_zc_timer_create(int(max_calls), ctypes.byref(h)))
         self.handle = h
+        self.stages = stages
 
     def read(self):
         """Synchronises on the events; returns (ncalls, {stage: total ms})."""
         n = ctypes.c_int()
-        ms = (ctypes.c_float * len(STAGES))()
+        ms = (ctypes.c_float * MAX_STAGES)()
         _check(lib().moe_zc_timer_read(self.handle, ctypes.byref(n), ms))
-        return n.value, dict(zip(STAGES, [float(v) for v in ms]))
+        return n.value, dict(zip(self.stages, [float(v) for v in ms]))
 
     def reset(self):
         lib().moe_zc_timer_reset(self.handle)
@@ -268,3 +278,51 @@ def forward_fp8(x, W_router, bias, W_gate, W_gate_exp, W_up, W_up_exp, W_down, W
         workspace.numel() * workspace.element_size(), stream,
         timer.handle if timer is not None else None))
     return out, counts, topk_idx, topk_gate
+
+
+# ---------------------------------------------------------------------------
+# Backward of the block
+# ---------------------------------------------------------------------------
+
+def backward_workspace_bytes(T, d, I, N, Z, k) -> int:
+    return int(lib().moe_zc_backward_workspace_bytes(
+        ctypes.byref(make_dims(T, d, I, N, Z, k, BF16))))
+
+
+def backward(x, W_router, W_gate, W_up, W_down, topk_idx, topk_gate, dout, N: int, Z: int, *,
+             dx=None, dW_router=None, dW_gate=None, dW_up=None, dW_down=None, workspace=None,
+             stream=None, timer: Optional[Timer] = None):
+    """moe_zc_backward on torch device tensors (bfloat16 x, weights and dout;
+    the forward's topk_idx int32 / topk_gate float32).  Returns (dx, dW_router,
+    dW_gate, dW_up, dW_down); the float32 weight gradients are accumulated
+    into the given tensors, else into new zero tensors."""
+    import torch
+
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    I = W_gate.shape[1] if (W_gate is not None and N > 0) else 0
+    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x))
+    dev = x.device
+    if dx is None:
+        dx = torch.empty_like(x)
+    z = lambda *shape: torch.zeros(shape, dtype=torch.float32, device=dev)  # noqa: E731
+    if dW_router is None:
+        dW_router = z(N + Z, d)
+    if N > 0:
+        if dW_gate is None:
+            dW_gate = z(N, I, d)
+        if dW_up is None:
+            dW_up = z(N, I, d)
+        if dW_down is None:
+            dW_down = z(N, d, I)
+    if workspace is None:
+        nbytes = int(lib().moe_zc_backward_workspace_bytes(ctypes.byref(dims)))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(lib().moe_zc_backward(
+        ctypes.byref(dims), _ptr(x), _ptr(W_router), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
+        _ptr(topk_idx), _ptr(topk_gate), _ptr(dout), _ptr(dx), _ptr(dW_router), _ptr(dW_gate),
+        _ptr(dW_up), _ptr(dW_down), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        stream, timer.handle if timer is not None else None))
+    return dx, dW_router, dW_gate, dW_up, dW_down

@@ -179,7 +179,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
   // ---- the 64 weight rows of this wave (MFMA A operand) -------------------
   const uint32_t wbytes = static_cast<uint32_t>(g.nrows) * static_cast<uint32_t>(K) * ES;
   int rowbase[2];  // first weight row of each 32-row block
-  if (MODE == MODE_GATE_UP) {
+  constexpr bool kGateUp = MODE == MODE_GATE_UP || MODE == MODE_GATE_UP_RAW;
+  if (kGateUp) {
     rowbase[0] = rowbase[1] = rb * 128 + wave * 32;  // block 0: W_gate, block 1: W_up
     st.ra[0] = make_rsrc(static_cast<const char *>(g.wa) + e * g.w_expert_stride * ES, wbytes);
     st.ra[1] = make_rsrc(static_cast<const char *>(g.wb) + e * g.w_expert_stride * ES, wbytes);
@@ -202,7 +203,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
 
   // ---- token rows (B operand): lane (lr, chunk) of wave w loads row
   // (4i + w)*8 + lr of the chunk in instruction i ------------------------
-  if (MODE == MODE_GATE_UP) {
+  if (kGateUp) {
     st.rb = make_rsrc(g.src, static_cast<uint32_t>(g.T) * K * ES);  // all of x (gathered)
   } else {
     st.rb = make_rsrc(static_cast<const char *>(g.src) + static_cast<int64_t>(m0) * K * ES,
@@ -213,7 +214,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
   for (int i = 0; i < NBR; ++i) {
     const int tr = (i * 4 + wave) * 8 + lr;
     uint32_t row = 0;
-    if (tr < mcount) row = MODE == MODE_GATE_UP ? static_cast<uint32_t>(g.tok[m0 + tr]) : tr;
+    if (tr < mcount) row = kGateUp ? static_cast<uint32_t>(g.tok[m0 + tr]) : tr;
     tvo[i] = tr < mcount ? row * K * ES + kbyte0 + chunk * 16 : kOOB;
   }
 
@@ -276,6 +277,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
             const int row = rowbase[a] + gi * 8 + h * 4 + j;
             if (row < g.nrows) orow[row] = acc[a][nb][gi * 4 + j];
           }
+    } else if (MODE == MODE_GATE_UP_RAW) {
+      // the two projections themselves (the backward's recomputation)
+      T *grow = static_cast<T *>(g.out) + (static_cast<int64_t>(m0) + col) * g.out_ld;
+      T *urow = static_cast<T *>(g.out2) + (static_cast<int64_t>(m0) + col) * g.out_ld;
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int row = rowbase[0] + gi * 8 + h * 4;
+        if (row < g.nrows) {
+          const floatx16 &ga = acc[0][nb];
+          const floatx16 &ua = acc[1][nb];
+          store4<T>(grow + row, ga[gi * 4 + 0], ga[gi * 4 + 1], ga[gi * 4 + 2], ga[gi * 4 + 3]);
+          store4<T>(urow + row, ua[gi * 4 + 0], ua[gi * 4 + 1], ua[gi * 4 + 2], ua[gi * 4 + 3]);
+        }
+      }
     } else if (MODE == MODE_GATE_UP) {
       T *orow = static_cast<T *>(g.out) + (static_cast<int64_t>(m0) + col) * g.out_ld;
 #pragma unroll
@@ -381,7 +396,9 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
 }
 
 // Weight rows one workgroup covers (GATE_UP: per matrix).
-static int rows_per_wg(int mode) { return mode == MODE_GATE_UP ? 128 : 256; }
+static int rows_per_wg(int mode) {
+  return mode == MODE_GATE_UP || mode == MODE_GATE_UP_RAW ? 128 : 256;
+}
 
 template <typename T, int MODE>
 static hipError_t launch_gemm_t(const GemmArgs &g, int nb, int64_t max_tiles, hipStream_t s) {
@@ -401,7 +418,8 @@ template <int MODE>
 static hipError_t launch_gemm(const Plan &p, const GemmArgs &g, int nb, int64_t max_tiles,
                               hipStream_t s) {
   if (p.dtype == MOE_ZC_BF16) return launch_gemm_t<bf16_t, MODE>(g, nb, max_tiles, s);
-  return launch_gemm_t<float, MODE>(g, nb, max_tiles, s);
+  if constexpr (MODE == MODE_GATE_UP_RAW) return hipErrorInvalidValue;  // bf16 only
+  else return launch_gemm_t<float, MODE>(g, nb, max_tiles, s);
 }
 
 // Upper bound of the GEMM chunks: sum_e ceil(M_e / MT) <= P / MT + min(N, P).
@@ -447,6 +465,30 @@ hipError_t launch_gate_up(const Plan &p, hipStream_t s) {
   g.N = p.N;
   g.split = 1;
   return launch_gemm<MODE_GATE_UP>(p, g, p.nbmax, max_chunks(p) * g.nrb, s);
+}
+
+// The backward's recomputation of both projections: G = X W_gate^T and
+// U = X W_up^T per expert ([P, I] each, the dims' dtype).
+hipError_t launch_gate_up_raw(const Plan &p, hipStream_t s) {
+  GemmArgs g = {};
+  g.wa = p.w_gate;
+  g.wb = p.w_up;
+  g.src = p.x;
+  g.tok = p.tok;
+  g.offs = p.offs;
+  g.chunk_off = p.chunk_off;
+  g.meta = p.meta;
+  g.out = p.bG;
+  g.out2 = p.bU;
+  g.w_expert_stride = static_cast<int64_t>(p.I) * p.d;
+  g.T = p.T;
+  g.K = p.d;
+  g.nrows = p.I;
+  g.out_ld = p.I;
+  g.nrb = (p.I + rows_per_wg(MODE_GATE_UP_RAW) - 1) / rows_per_wg(MODE_GATE_UP_RAW);
+  g.N = p.N;
+  g.split = 1;
+  return launch_gemm<MODE_GATE_UP_RAW>(p, g, p.nbmax, max_chunks(p) * g.nrb, s);
 }
 
 hipError_t launch_down(const Plan &p, hipStream_t s) {

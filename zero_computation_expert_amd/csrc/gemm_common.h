@@ -17,7 +17,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-enum { MODE_ROUTER = 0, MODE_GATE_UP = 1, MODE_DOWN = 2 };
+// GATE_UP_RAW: the gate/up GEMM writing both projections (G to out, U to
+// out2) instead of their SwiGLU, for the backward.
+enum { MODE_ROUTER = 0, MODE_GATE_UP = 1, MODE_DOWN = 2, MODE_GATE_UP_RAW = 3 };
 
 struct GemmArgs {
   const void *wa;   // ROUTER: W_router; GATE_UP: W_gate; DOWN: W_down
@@ -27,7 +29,8 @@ struct GemmArgs {
   const int32_t *offs;       // [N+1] permuted row offsets (GATE_UP, DOWN)
   const int32_t *chunk_off;  // [N+1] chunk prefix (GATE_UP, DOWN)
   const int32_t *meta;       // meta[0] = total chunks (GATE_UP, DOWN)
-  void *out;                 // logits (f32) / H / Y
+  void *out;                 // logits (f32) / H / Y / G (GATE_UP_RAW)
+  void *out2;                // GATE_UP_RAW: U
   int64_t w_expert_stride;   // elements between experts' matrices
   int64_t T;                 // tokens (ROUTER: chunking; GATE_UP: rows of x)
   int K;                     // reduction length
@@ -170,26 +173,33 @@ struct TileLoc {
 // each expert's first chunk.  The expert of chunk c is the last e with
 // chunk_off[e] <= c (a uniform binary search over the small prefix table,
 // read through the caches).
-__device__ __forceinline__ TileLoc locate_expert_tile(const GemmArgs &g, int v, int MT) {
+__device__ __forceinline__ TileLoc locate_segment_tile(const int32_t *offs,
+                                                       const int32_t *chunk_off, int N, int nrb,
+                                                       int v, int MT) {
   TileLoc t;
   t.k0 = 0;
-  t.klen = g.K;
+  t.klen = 0;
   t.s = 0;
-  const int c = v / g.nrb;
-  const int32_t *co = g.chunk_off;
-  int lo = 0, hi = g.N - 1;
+  const int c = v / nrb;
+  int lo = 0, hi = N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (co[mid] <= c) lo = mid;
+    if (chunk_off[mid] <= c) lo = mid;
     else hi = mid - 1;
   }
   t.e = lo;
-  const int local = v - g.nrb * co[t.e];
-  const int nch = co[t.e + 1] - co[t.e];
+  const int local = v - nrb * chunk_off[t.e];
+  const int nch = chunk_off[t.e + 1] - chunk_off[t.e];
   t.rb = local / nch;
   const int ch = local - t.rb * nch;
-  t.m0 = g.offs[t.e] + ch * MT;
-  t.mcount = min(MT, g.offs[t.e + 1] - t.m0);
+  t.m0 = offs[t.e] + ch * MT;
+  t.mcount = min(MT, offs[t.e + 1] - t.m0);
+  return t;
+}
+
+__device__ __forceinline__ TileLoc locate_expert_tile(const GemmArgs &g, int v, int MT) {
+  TileLoc t = locate_segment_tile(g.offs, g.chunk_off, g.N, g.nrb, v, MT);
+  t.klen = g.K;
   return t;
 }
 

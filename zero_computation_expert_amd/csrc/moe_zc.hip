@@ -110,7 +110,8 @@ static bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 struct moe_zc_timer {
   int max_calls;
   int ncalls;
-  hipEvent_t *ev;  // [max_calls][MOE_ZC_NSTAGES + 1]
+  hipEvent_t *ev;  // [max_calls][MOE_ZC_MAX_STAGES + 1]
+  int *nst;        // [max_calls] stages recorded by each call
 };
 
 using namespace moezc;
@@ -205,8 +206,9 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   if (topk_gate) p.gate = topk_gate;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t *ev = timer ? timer->ev + static_cast<size_t>(timer->ncalls) * (MOE_ZC_NSTAGES + 1)
+  hipEvent_t *ev = timer ? timer->ev + static_cast<size_t>(timer->ncalls) * (MOE_ZC_MAX_STAGES + 1)
                          : nullptr;
+  if (timer) timer->nst[timer->ncalls] = MOE_ZC_NSTAGES;
   auto mark = [&](int i) -> bool {
     return ev == nullptr || hipEventRecord(ev[i], s) == hipSuccess;
   };
@@ -240,6 +242,186 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
     const bool ffn = i == MOE_ZC_STAGE_GATE_UP || i == MOE_ZC_STAGE_DOWN;
     if (!(ffn && p.N == 0))
       if (run[i](p, s) != hipSuccess) return MOE_ZC_EHIP;
+    if (!mark(i + 1)) return MOE_ZC_EHIP;
+  }
+  if (timer) timer->ncalls++;
+  return MOE_ZC_OK;
+}
+
+// ---- backward -------------------------------------------------------------
+// Workspace of the backward; with base == nullptr only sizes.
+static size_t layout_bwd(const moe_zc_dims *dm, char *base, Plan *p) {
+  const int64_t T = dm->T;
+  const int E = dm->N + dm->Z;
+  const int64_t nblk = (T + kTokPerBlk - 1) / kTokPerBlk;
+  const int64_t pmax = T * std::min(dm->k, dm->N);
+  const int I = dm->N > 0 ? dm->I : 0;
+  const int ldl = (E + 7) / 8 * 8;
+  const int nrbi = (I + 255) / 256;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *ptr = base ? base + off : nullptr;
+    off = align_up(off + bytes);
+    return ptr;
+  };
+  const RouterSplit rs = router_split(T, dm->d, E, MOE_ZC_BF16);
+  char *logits = take(static_cast<size_t>(rs.split) * T * E * 4);
+  char *blockhist = take(static_cast<size_t>(nblk) * E * 4);
+  char *counts = take(static_cast<size_t>(E) * 4);
+  char *offs = take(static_cast<size_t>(dm->N + 1) * 4);
+  char *chunk_off = take(static_cast<size_t>(dm->N + 1) * 4);
+  char *meta = take(64);
+  char *idx = take(static_cast<size_t>(T) * dm->k * 4);
+  char *rowmap = take(static_cast<size_t>(T) * dm->k * 4);
+  char *tok = take(static_cast<size_t>(pmax) * 4);
+  char *gate_perm = take(static_cast<size_t>(pmax) * 4);
+  char *bG = take(static_cast<size_t>(pmax) * I * 2);
+  char *bU = take(static_cast<size_t>(pmax) * I * 2);
+  char *bH = take(static_cast<size_t>(pmax) * I * 2);
+  char *dpart = take(static_cast<size_t>(nrbi) * pmax * 4);
+  char *dl = take(static_cast<size_t>(T) * ldl * 2);
+  char *xp = take(static_cast<size_t>(pmax) * dm->d * 2);
+  char *dyp = take(static_cast<size_t>(pmax) * dm->d * 2);
+  char *dxp = take(static_cast<size_t>(pmax) * dm->d * 2);
+  char *dxr = take(static_cast<size_t>(T) * dm->d * 4);
+  if (p) {
+    p->rs = rs;
+    p->logits = reinterpret_cast<float *>(logits);
+    p->blockhist = reinterpret_cast<int32_t *>(blockhist);
+    p->counts = reinterpret_cast<int32_t *>(counts);
+    p->offs = reinterpret_cast<int32_t *>(offs);
+    p->chunk_off = reinterpret_cast<int32_t *>(chunk_off);
+    p->meta = reinterpret_cast<int32_t *>(meta);
+    p->idx = reinterpret_cast<int32_t *>(idx);
+    p->rowmap = reinterpret_cast<int32_t *>(rowmap);
+    p->tok = reinterpret_cast<int32_t *>(tok);
+    p->gate_perm = reinterpret_cast<float *>(gate_perm);
+    p->bG = bG;
+    p->bU = bU;
+    p->bH = bH;
+    p->dpart = reinterpret_cast<float *>(dpart);
+    p->dl = dl;
+    p->ldl = ldl;
+    p->xp = xp;
+    p->dyp = dyp;
+    p->dxp = dxp;
+    p->dxr = reinterpret_cast<float *>(dxr);
+  }
+  return off;
+}
+
+static bool bwd_dims_ok(const moe_zc_dims *dm, int *status) {
+  if (!dims_ok(dm, status)) return false;
+  if (dm->dtype != MOE_ZC_BF16) {
+    *status = MOE_ZC_EDTYPE;
+    return false;
+  }
+  // W_router, the router-logit gradient and an expert's rows of dG / dU / H
+  // are addressed through 32-bit buffer offsets (x, dout and one expert
+  // matrix are bounded by dims_ok)
+  const int64_t E = static_cast<int64_t>(dm->N) + dm->Z;
+  const int64_t lim = int64_t(1) << 31;
+  if (E * dm->d * 2 >= lim || dm->T * ((E + 7) / 8 * 8) * 2 >= lim ||
+      (dm->N > 0 && dm->T * dm->I * 2 >= lim)) {
+    *status = MOE_ZC_EINVAL;
+    return false;
+  }
+  return true;
+}
+
+static int backward_impl(const moe_zc_dims *dm, const void *x, const void *w_router,
+                         const void *w_gate, const void *w_up, const void *w_down,
+                         const int32_t *topk_idx, const float *topk_gate, const void *dout,
+                         void *dx, float *dw_router, float *dw_gate, float *dw_up,
+                         float *dw_down, void *workspace, size_t workspace_bytes, void *stream,
+                         moe_zc_timer *timer) {
+  int st;
+  if (!bwd_dims_ok(dm, &st)) return st;
+  const int64_t T = dm->T;
+  const size_t xbytes = static_cast<size_t>(T) * dm->d * 2;
+  if (T > 0) {
+    if (!x || !w_router || !topk_idx || !topk_gate || !dout || !dx || !dw_router)
+      return MOE_ZC_EINVAL;
+    if (dm->N > 0 && (!w_gate || !w_up || !w_down || !dw_gate || !dw_up || !dw_down))
+      return MOE_ZC_EINVAL;
+    if (overlap(dx, xbytes, x, xbytes) || overlap(dx, xbytes, dout, xbytes)) return MOE_ZC_EINVAL;
+  }
+  const void *p16[] = {x, w_router, w_gate, w_up, w_down, dout, dx};
+  for (const void *ptr : p16)
+    if (ptr && !aligned(ptr, 16)) return MOE_ZC_EALIGN;
+  const void *p4[] = {topk_idx, topk_gate, dw_router, dw_gate, dw_up, dw_down};
+  for (const void *ptr : p4)
+    if (ptr && !aligned(ptr, 4)) return MOE_ZC_EALIGN;
+  const size_t need = layout_bwd(dm, nullptr, nullptr);
+  if (T > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MOE_ZC_ENOSPC;
+    if (!aligned(workspace, 256)) return MOE_ZC_EALIGN;
+  }
+  if (timer && timer->ncalls >= timer->max_calls) return MOE_ZC_ENOSPC;
+
+  Plan p = {};
+  p.T = T;
+  p.d = dm->d;
+  p.I = dm->N > 0 ? dm->I : 0;
+  p.N = dm->N;
+  p.Z = dm->Z;
+  p.E = dm->N + dm->Z;
+  p.k = dm->k;
+  p.dtype = MOE_ZC_BF16;
+  p.nblk = static_cast<int>((T + kTokPerBlk - 1) / kTokPerBlk);
+  p.pmax = T * std::min(dm->k, dm->N);
+  const int64_t avg_rows = dm->N > 0 ? p.pmax / dm->N : 0;
+  p.nbmax = avg_rows >= 96 ? 5 : (avg_rows >= 24 ? 4 : 1);
+  p.x = x;
+  p.w_router = w_router;
+  p.w_gate = w_gate;
+  p.w_up = w_up;
+  p.w_down = w_down;
+  p.idx_in = topk_idx;
+  p.gate = const_cast<float *>(topk_gate);
+  p.dout = dout;
+  p.dx = dx;
+  p.dw_router = dw_router;
+  p.dw_gate = dw_gate;
+  p.dw_up = dw_up;
+  p.dw_down = dw_down;
+  layout_bwd(dm, static_cast<char *>(workspace), &p);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t *ev = timer ? timer->ev + static_cast<size_t>(timer->ncalls) * (MOE_ZC_MAX_STAGES + 1)
+                         : nullptr;
+  if (timer) timer->nst[timer->ncalls] = MOE_ZC_BWD_NSTAGES;
+  auto mark = [&](int i) -> bool {
+    return ev == nullptr || hipEventRecord(ev[i], s) == hipSuccess;
+  };
+  if (T == 0) {
+    if (timer) {
+      for (int i = 0; i <= MOE_ZC_BWD_NSTAGES; ++i)
+        if (!mark(i)) return MOE_ZC_EHIP;
+      timer->ncalls++;
+    }
+    return MOE_ZC_OK;
+  }
+  typedef hipError_t (*Launch)(const Plan &, hipStream_t);
+  const Launch stages[MOE_ZC_BWD_NSTAGES] = {
+      [](const Plan &q, hipStream_t ss) {  // routing bookkeeping, permuted rows
+        hipError_t e = launch_bwd_route(q, ss);
+        return (e != hipSuccess || q.N == 0) ? e : launch_bwd_gather(q, ss);
+      },
+      launch_router_gemm, launch_gate_up_raw, launch_dgrad_v, launch_router_bwd,
+      launch_wgrad_down, launch_wgrad_gate_up, launch_dgrad_x,
+      [](const Plan &q, hipStream_t ss) {  // dx: router part, then the gather
+        hipError_t e = launch_dgrad_router(q, ss);
+        return e != hipSuccess ? e : launch_dx_gather(q, ss);
+      },
+      launch_wgrad_router};
+  if (!mark(0)) return MOE_ZC_EHIP;
+  for (int i = 0; i < MOE_ZC_BWD_NSTAGES; ++i) {
+    const bool ffn = i == MOE_ZC_BSTAGE_RECOMPUTE || i == MOE_ZC_BSTAGE_DGRAD_V ||
+                     i == MOE_ZC_BSTAGE_WGRAD_DOWN || i == MOE_ZC_BSTAGE_WGRAD_GATE_UP ||
+                     i == MOE_ZC_BSTAGE_DGRAD_X;
+    if (!(ffn && p.N == 0))
+      if (stages[i](p, s) != hipSuccess) return MOE_ZC_EHIP;
     if (!mark(i + 1)) return MOE_ZC_EHIP;
   }
   if (timer) timer->ncalls++;
@@ -289,6 +471,22 @@ int moe_zc_forward_timed(const moe_zc_dims *dims, const void *x, const void *W_r
                       topk_gate, workspace, workspace_bytes, stream, timer);
 }
 
+size_t moe_zc_backward_workspace_bytes(const moe_zc_dims *dims) {
+  int st;
+  if (!bwd_dims_ok(dims, &st)) return 0;
+  return layout_bwd(dims, nullptr, nullptr);
+}
+
+int moe_zc_backward(const moe_zc_dims *dims, const void *x, const void *W_router,
+                    const void *W_gate, const void *W_up, const void *W_down,
+                    const int32_t *topk_idx, const float *topk_gate, const void *dout, void *dx,
+                    float *dW_router, float *dW_gate, float *dW_up, float *dW_down,
+                    void *workspace, size_t workspace_bytes, void *stream, moe_zc_timer *timer) {
+  return backward_impl(dims, x, W_router, W_gate, W_up, W_down, topk_idx, topk_gate, dout, dx,
+                       dW_router, dW_gate, dW_up, dW_down, workspace, workspace_bytes, stream,
+                       timer);
+}
+
 const char *moe_zc_status_string(int status) {
   switch (status) {
     case MOE_ZC_OK: return "ok";
@@ -306,9 +504,12 @@ int moe_zc_timer_create(int max_calls, moe_zc_timer **out) {
   *out = nullptr;
   moe_zc_timer *t = new (std::nothrow) moe_zc_timer;
   if (!t) return MOE_ZC_EINVAL;
-  const size_t n = static_cast<size_t>(max_calls) * (MOE_ZC_NSTAGES + 1);
+  const size_t n = static_cast<size_t>(max_calls) * (MOE_ZC_MAX_STAGES + 1);
   t->ev = new (std::nothrow) hipEvent_t[n];
-  if (!t->ev) {
+  t->nst = new (std::nothrow) int[static_cast<size_t>(max_calls)];
+  if (!t->ev || !t->nst) {
+    delete[] t->ev;
+    delete[] t->nst;
     delete t;
     return MOE_ZC_EINVAL;
   }
@@ -318,6 +519,7 @@ int moe_zc_timer_create(int max_calls, moe_zc_timer **out) {
     if (hipEventCreate(&t->ev[i]) != hipSuccess) {
       for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(t->ev[j]);
       delete[] t->ev;
+      delete[] t->nst;
       delete t;
       return MOE_ZC_EHIP;
     }
@@ -328,11 +530,12 @@ int moe_zc_timer_create(int max_calls, moe_zc_timer **out) {
 
 int moe_zc_timer_read(moe_zc_timer *t, int *ncalls, float *ms) {
   if (t == nullptr || ms == nullptr) return MOE_ZC_EINVAL;
-  for (int s = 0; s < MOE_ZC_NSTAGES; ++s) ms[s] = 0.0f;
+  for (int s = 0; s < MOE_ZC_MAX_STAGES; ++s) ms[s] = 0.0f;
   for (int c = 0; c < t->ncalls; ++c) {
-    hipEvent_t *ev = t->ev + static_cast<size_t>(c) * (MOE_ZC_NSTAGES + 1);
-    if (hipEventSynchronize(ev[MOE_ZC_NSTAGES]) != hipSuccess) return MOE_ZC_EHIP;
-    for (int s = 0; s < MOE_ZC_NSTAGES; ++s) {
+    hipEvent_t *ev = t->ev + static_cast<size_t>(c) * (MOE_ZC_MAX_STAGES + 1);
+    const int ns = t->nst[c];
+    if (hipEventSynchronize(ev[ns]) != hipSuccess) return MOE_ZC_EHIP;
+    for (int s = 0; s < ns; ++s) {
       float v = 0.0f;
       if (hipEventElapsedTime(&v, ev[s], ev[s + 1]) != hipSuccess) return MOE_ZC_EHIP;
       ms[s] += v;
@@ -348,9 +551,10 @@ void moe_zc_timer_reset(moe_zc_timer *t) {
 
 void moe_zc_timer_destroy(moe_zc_timer *t) {
   if (!t) return;
-  const size_t n = static_cast<size_t>(t->max_calls) * (MOE_ZC_NSTAGES + 1);
+  const size_t n = static_cast<size_t>(t->max_calls) * (MOE_ZC_MAX_STAGES + 1);
   for (size_t i = 0; i < n; ++i) (void)hipEventDestroy(t->ev[i]);
   delete[] t->ev;
+  delete[] t->nst;
   delete t;
 }
 

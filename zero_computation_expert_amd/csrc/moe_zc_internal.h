@@ -132,6 +132,18 @@ hipError_t launch_zero_counts(const Plan &p, hipStream_t s);
 hipError_t launch_quant_x(const Plan &p, hipStream_t s);
 hipError_t launch_gate_up8(const Plan &p, hipStream_t s);
 hipError_t launch_down8(const Plan &p, hipStream_t s);
+// backward
+hipError_t launch_bwd_route(const Plan &p, hipStream_t s);      // idx -> counts, permutation
+hipError_t launch_bwd_gather(const Plan &p, hipStream_t s);     // x and gate*dout rows, permuted
+hipError_t launch_gate_up_raw(const Plan &p, hipStream_t s);    // G, U
+hipError_t launch_dgrad_v(const Plan &p, hipStream_t s);        // dG, dU, H, dgate partials
+hipError_t launch_router_bwd(const Plan &p, hipStream_t s);     // dl
+hipError_t launch_wgrad_down(const Plan &p, hipStream_t s);
+hipError_t launch_wgrad_gate_up(const Plan &p, hipStream_t s);
+hipError_t launch_dgrad_x(const Plan &p, hipStream_t s);        // permuted dx rows
+hipError_t launch_dgrad_router(const Plan &p, hipStream_t s);   // router part of dx
+hipError_t launch_dx_gather(const Plan &p, hipStream_t s);      // dx
+hipError_t launch_wgrad_router(const Plan &p, hipStream_t s);
 
 // Everything one forward call needs, resolved on the host.
 struct Plan {
@@ -168,6 +180,18 @@ struct Plan {
   uint8_t *sx;          // FP8 path: [T, d/128] exponents of x
   uint8_t *sxp;         // FP8 path: [pmax, d/128] the same, rows in permuted order
   uint8_t *sh;          // FP8 path: [pmax, I/128] exponents of H
+  // backward (moe_zc_backward); idx then holds the sanitized routing
+  const void *dout;     // [T, d] output gradient
+  void *dx;             // [T, d] input gradient
+  float *dw_router, *dw_gate, *dw_up, *dw_down;  // fp32, accumulated into
+  const int32_t *idx_in;  // the caller's routing
+  float *gate_perm;     // [pmax] gate of each permuted row
+  void *bG, *bU, *bH;   // [pmax, I] G and U (then dG and dU), H
+  float *dpart;         // [ceil(I/256), pmax] partial dgate sums
+  void *dl;             // [T, ldl] router-logit gradient, bf16 (zero padded)
+  int ldl;              // E rounded up to 8
+  void *xp, *dyp, *dxp; // [pmax, d] x, gate*dout and dx rows in permuted order
+  float *dxr;           // [T, d] router part of dx
 };
 
 }  // namespace moezc

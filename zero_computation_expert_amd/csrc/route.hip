@@ -227,12 +227,16 @@ __global__ void __launch_bounds__(1024) expert_scan_kernel(const int32_t *__rest
 // tokens routed to e).  One wave per block of kTokPerBlk tokens; tokens are
 // walked in order, lanes are slots (the k experts of a token are distinct,
 // so the lanes never touch the same counter at once).
+// Negative entries (slots the backward's sanitizing dropped) map to no row.
+// gate_perm (nullable) receives each permuted row's gate.
 __global__ void __launch_bounds__(64) permute_kernel(const int32_t *__restrict__ idx, int64_t T,
                                                      int k, int N, int E,
                                                      const int32_t *__restrict__ offs,
                                                      const int32_t *__restrict__ blockhist,
                                                      int32_t *__restrict__ rowmap,
-                                                     int32_t *__restrict__ tok) {
+                                                     int32_t *__restrict__ tok,
+                                                     const float *__restrict__ gate,
+                                                     float *__restrict__ gate_perm) {
   __shared__ int s_next[kMaxE];
   __shared__ int s_idx[kTokPerBlk * kMaxK];
   const int lane = threadIdx.x;
@@ -246,10 +250,11 @@ __global__ void __launch_bounds__(64) permute_kernel(const int32_t *__restrict__
     if (lane < k) {
       const int e = s_idx[tt * k + lane];
       int r = -1;
-      if (e < N) {
+      if (e >= 0 && e < N) {
         r = s_next[e];
         s_next[e] = r + 1;
         tok[r] = static_cast<int32_t>(t0 + tt);
+        if (gate_perm) gate_perm[r] = gate[(t0 + tt) * k + lane];
       }
       rowmap[(t0 + tt) * k + lane] = r;
     }
@@ -289,7 +294,7 @@ hipError_t launch_scan(const Plan &p, hipStream_t s) {
 
 hipError_t launch_permute(const Plan &p, hipStream_t s) {
   hipLaunchKernelGGL(permute_kernel, dim3(p.nblk), dim3(64), 0, s, p.idx, p.T, p.k, p.N, p.E,
-                     p.offs, p.blockhist, p.rowmap, p.tok);
+                     p.offs, p.blockhist, p.rowmap, p.tok, p.gate, p.gate_perm);
   return hipGetLastError();
 }
 
