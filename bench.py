@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--fp8", action="store_true",
                     help="block-scaled FP8 experts (moe_zc_forward_fp8); a separate line, "
                          "not the bf16 headline")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_zc_backward (the block's backward with fp32 weight-gradient "
+                         "accumulation); a separate line, not the forward headline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -149,6 +152,153 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
+def backward_algorithmic(cfg, counts):
+    """Algorithmic HBM bytes and FLOPs of the backward, per stage and per step:
+    weights read once per touched expert, fp32 weight gradients read and
+    written once, x / dout read, dx written (intermediates not counted)."""
+    import numpy as np
+
+    cnt = np.asarray(counts, dtype=np.int64)
+    P = int(cnt[: cfg.N].sum())
+    tch = int((cnt[: cfg.N] > 0).sum())
+    T, d, I, E, k = cfg.T, cfg.d, cfg.I, cfg.E, cfg.k
+    w2, g4 = d * I * 2, d * I * 4
+    st = {
+        "router": (T * d * 2 + E * d * 2, 2 * T * d * E),
+        "recompute": (tch * 2 * w2 + T * d * 2, 4 * P * d * I),
+        "dgrad_v": (tch * w2 + T * d * 2, 2 * P * d * I),
+        "wgrad_down": (tch * 2 * g4, 2 * P * d * I),
+        "wgrad_gate_up": (2 * tch * 2 * g4, 4 * P * d * I),
+        "dgrad_x": (tch * 2 * w2, 4 * P * d * I),
+        "dx": (E * d * 2 + 2 * T * d * 2, 2 * T * E * d),
+        "wgrad_router": (2 * E * d * 4 + T * d * 2, 2 * T * E * d),
+    }
+    step_bytes = 3 * T * d * 2 + E * d * 2 + 3 * tch * w2 + 3 * tch * 2 * g4 + 2 * E * d * 4 + T * k * 8
+    step_flops = 2 * 2 * T * d * E + (4 + 2 + 2 + 4 + 4) * P * d * I
+    return {"P": P, "touched": tch, "stages": st, "step_bytes": step_bytes,
+            "step_flops": step_flops}
+
+
+def backward_cpu_baseline(cfg, inp, idx, gate, dout, ntok):
+    """The oracle's per-token backward on the first ntok tokens (16 threads;
+    the experts those tokens use are copied from the device generator's
+    tensors, untimed).  It computes dx, the gate and router-logit gradients
+    and the per-slot dg/du/h, but not the weight-gradient accumulation, so it
+    overstates the oracle's rate for the whole backward."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    import synth
+    from tests import _parity as P
+
+    t0 = time.time()
+    x = P.to_np(inp["x"][:ntok])
+    wr = P.to_np(inp["W_router"])
+    idx_h, gate_h = idx[:ntok].cpu().numpy(), gate[:ntok].cpu().numpy()
+    dout_h = synth.bf16_bits_to_f32(P.to_np(dout[:ntok]))
+    used = sorted({int(e) for e in idx_h.ravel() if e < cfg.N})
+    experts = {e: (P.to_np(inp["W_gate"][e]), P.to_np(inp["W_up"][e]), P.to_np(inp["W_down"][e]))
+               for e in used}
+    prep = time.time() - t0
+    threads = min(16, ntok)
+
+    def one(t):
+        return oracle.token_backward(x[t], "bf16", wr, cfg.N, idx_h[t], gate_h[t], dout_h[t],
+                                     {e: experts[e] for e in idx_h[t] if e < cfg.N})
+
+    t1 = time.time()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, range(ntok)))
+    sec = time.time() - t1
+    return {"value": ntok / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {ntok} of {cfg.T} tokens, oracle per-token backward (dx, gate and "
+                      f"router-logit gradients; weight-gradient accumulation not included, so "
+                      f"this overstates the CPU rate); {sec:.1f}s on {threads} threads of a "
+                      f"{cpu_model()}, {prep:.1f}s input copy excluded"}
+
+
+def backward_bench(args, cfg, inp, dev):
+    import torch
+
+    import synth
+    import zero_computation_expert_amd as moe
+
+    if cfg.dtype != "bf16":
+        print("the backward is bfloat16 only", file=sys.stderr)
+        sys.exit(2)
+    # routing from one untimed forward
+    _, counts, idx, gate = moe.forward(inp["x"], inp["W_router"], inp["bias"], inp["W_gate"],
+                                       inp["W_up"], inp["W_down"], cfg.N, cfg.Z, cfg.k)
+    dout = synth.device_dout(cfg, dev)
+    z = lambda *shape: torch.zeros(shape, dtype=torch.float32, device=dev)  # noqa: E731
+    g = {"dW_router": z(cfg.E, cfg.d), "dW_gate": z(cfg.N, cfg.I, cfg.d),
+         "dW_up": z(cfg.N, cfg.I, cfg.d), "dW_down": z(cfg.N, cfg.d, cfg.I)}
+    nb = moe.backward_workspace_bytes(cfg.T, cfg.d, cfg.I, cfg.N, cfg.Z, cfg.k)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    dx = torch.empty_like(inp["x"])
+    a = (inp["x"], inp["W_router"], inp["W_gate"], inp["W_up"], inp["W_down"], idx, gate, dout,
+         cfg.N, cfg.Z)
+    kw = dict(dx=dx, workspace=ws, **g)
+    for _ in range(args.warmup):
+        moe.backward(*a, **kw)
+    torch.cuda.synchronize()
+    timer = moe.Timer(max(1, args.steps), stages=moe.BWD_STAGES)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        moe.backward(*a, **kw, timer=timer)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    ncalls, stage_ms = timer.read()
+    timer.close()
+    sa = {k: v / ncalls for k, v in stage_ms.items()}
+    print(f"[bench] backward {args.steps} steps: {ms:.3f} ms/step; stages " +
+          " ".join(f"{k}={v:.3f}" for k, v in sa.items()), file=sys.stderr, flush=True)
+    alg = backward_algorithmic(cfg, counts.cpu().numpy())
+    kernels = {}
+    for name, (byt, fl) in alg["stages"].items():
+        sec = sa[name] / 1e3
+        kernels[name] = {"ms": round(sa[name], 4), "GB/s": round(byt / sec / 1e9, 1),
+                         "TFLOP/s": round(fl / sec / 1e12, 1),
+                         "hbm_frac": round(byt / sec / 1e9 / HBM_PEAK_GBS, 4),
+                         "mfma_frac": round(fl / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    # dominant kernel: the gate/up weight-gradient GEMM (two launches per
+    # step, dW_gate then dW_up, equal bytes)
+    per_launch = alg["stages"]["wgrad_gate_up"][0] // 2
+    launch_ms = sa["wgrad_gate_up"] / 2
+    gbs = per_launch / (launch_ms / 1e3) / 1e9
+    step_s = ms / 1e3
+    res = {
+        "metric": "MoE-layer backward tokens/s at 1 MI355X (dx and fp32 weight gradients)",
+        "value": round(cfg.T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 operands, fp32 accumulation and fp32 weight gradients",
+        "data": "synthetic (seeded Philox4x64 normals; random-init weights)",
+        "config": {"workload": f"{cfg.name} backward: T={cfg.T} d={cfg.d} I={cfg.I} N={cfg.N} "
+                               f"Z={cfg.Z} k={cfg.k} bf16",
+                   "ffn_pairs": alg["P"], "touched_experts": alg["touched"]},
+        "roofline": {"bound": "hbm", "kernel": "wgrad_kernel (dW_gate += dG^T X, dW_up += dU^T X; "
+                     "fp32 read-modify-write of the gradient)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": per_launch,
+                     "avg_launch_ms": round(launch_ms, 4)},
+        "step_hbm_frac": round(alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "step_mfma_frac": round(alg["step_flops"] / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "stages_ms": {k: round(v, 4) for k, v in sa.items()},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = backward_cpu_baseline(cfg, inp, idx, gate, dout,
+                                                    args.cpu_tokens or 16)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -176,6 +326,9 @@ def main():
     print(f"[bench] inputs for {cfg.name} generated on device in {time.time() - t0:.1f}s",
           file=sys.stderr, flush=True)
     dt_code = moe.BF16 if cfg.dtype == "bf16" else moe.F32
+    if args.backward:
+        backward_bench(args, cfg, inp, dev)
+        return
     if args.fp8:
         # quantize the expert weights once, untimed ([128,128] blocks), and
         # drop the bf16 copies

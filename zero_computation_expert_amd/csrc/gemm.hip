@@ -213,9 +213,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
 #pragma unroll
   for (int i = 0; i < NBR; ++i) {
     const int tr = (i * 4 + wave) * 8 + lr;
-    uint32_t row = 0;
-    if (tr < mcount) row = kGateUp ? static_cast<uint32_t>(g.tok[m0 + tr]) : tr;
-    tvo[i] = tr < mcount ? row * K * ES + kbyte0 + chunk * 16 : kOOB;
+    // The index load is clamped and its value always used (rows past the
+    // chunk get kOOB added: an offset past every buffer's range), so the
+    // compiler cannot sink it under a branch, and the NBR loads issue
+    // together instead of one round trip each.
+    const uint32_t row = kGateUp ? static_cast<uint32_t>(g.tok[m0 + min(tr, mcount - 1)])
+                                 : static_cast<uint32_t>(tr);
+    tvo[i] = row * K * ES + kbyte0 + chunk * 16 + (tr < mcount ? 0u : kOOB);
   }
 
   const int nks = (t.klen + KC - 1) / KC;

@@ -276,9 +276,11 @@ __device__ __forceinline__ void dgrad_tile(const DgradArgs &g, const TileLoc &t,
 #pragma unroll
   for (int i = 0; i < NBR; ++i) {
     const int tr = (i * 4 + wave) * 8 + lr;
-    uint32_t row = 0;
-    if (tr < t.mcount) row = MODE == BW_V ? static_cast<uint32_t>(g.tok[t.m0 + tr]) : tr;
-    b.off[i] = tr < t.mcount ? row * g.ldb * 2 + chunk * 16 : kOOB;
+    // clamped index load whose value is always used (kOOB added for rows
+    // past the tile), so the NBR loads issue together
+    const uint32_t row = MODE == BW_V ? static_cast<uint32_t>(g.tok[t.m0 + min(tr, t.mcount - 1)])
+                                      : static_cast<uint32_t>(tr);
+    b.off[i] = row * g.ldb * 2 + chunk * 16 + (tr < t.mcount ? 0u : kOOB);
   }
   char *const w[3] = {s_w[0] + wave * kWaveRowBytes, s_w[1] + wave * kWaveRowBytes,
                       s_w[2] + wave * kWaveRowBytes};
@@ -292,41 +294,70 @@ __device__ __forceinline__ void dgrad_tile(const DgradArgs &g, const TileLoc &t,
   // ---- epilogue: lane (r, h) holds column r, rows gi*8 + h*4 + [0, 4) ----
   if (MODE == BW_V) {
     float *s_part = reinterpret_cast<float *>(w[0]);  // this wave's own slot region
+    // G, U (read, then overwritten by dG, dU) and H: this tile's rows through
+    // buffer descriptors, edges by out-of-range offsets, every load of the
+    // epilogue issued before the first use
+    const int64_t rb0 = static_cast<int64_t>(t.m0) * g.M;
+    const uint32_t rbytes = static_cast<uint32_t>(t.mcount) * g.M * 2;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(g.gbuf + rb0, rbytes);
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(g.ubuf + rb0, rbytes);
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(g.hbuf + rb0, rbytes);
+    auto eoff = [&](int nb, int a2, int gi) -> uint32_t {
+      const int col = nb * 32 + r;
+      const int i0 = m_base + a2 * 32 + gi * 8 + h * 4;
+      return (col < t.mcount && i0 < g.M) ? static_cast<uint32_t>(col * g.M + i0) * 2u : kOOB;
+    };
+    // two-deep pipeline over the 32-column blocks: the loads of block nb + 1
+    // are issued before block nb is processed
+    uint2 gv[2][8], uv[2][8];
+    float gt[2];
+    auto issue = [&](int nb, int buf) {
+      gt[buf] = g.gate_perm[t.m0 + min(nb * 32 + r, t.mcount - 1)];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int o = static_cast<int>(eoff(nb, q >> 2, q & 3));
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rg, o, 0, 0);
+        const auto y = __builtin_amdgcn_raw_buffer_load_b64(ru, o, 0, 0);
+        gv[buf][q] = make_uint2(x[0], x[1]);
+        uv[buf][q] = make_uint2(y[0], y[1]);
+      }
+    };
+    issue(0, 0);
 #pragma unroll
     for (int nb = 0; nb < NBR; ++nb) {
-      const int col = nb * 32 + r;
-      const bool live = col < t.mcount;
-      const int64_t row = static_cast<int64_t>(t.m0) + (live ? col : 0);
-      const float gt = live ? g.gate_perm[row] : 0.0f;
+      const int cur = nb & 1;
+      if (nb + 1 < NBR) issue(nb + 1, cur ^ 1);
       float dsum = 0.0f;
 #pragma unroll
-      for (int a2 = 0; a2 < 2; ++a2)
+      for (int q = 0; q < 8; ++q) {
+        const int a2 = q >> 2, gi = q & 3;
+        const uint32_t gw[2] = {gv[cur][q].x, gv[cur][q].y}, uw[2] = {uv[cur][q].x, uv[cur][q].y};
+        float dg[4], du[4], hh[4];
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const int i0 = m_base + a2 * 32 + gi * 8 + h * 4;
-          if (!live || i0 >= g.M) continue;
-          const int64_t o = row * g.M + i0;
-          const uint2 gv = *reinterpret_cast<const uint2 *>(g.gbuf + o);
-          const uint2 uv = *reinterpret_cast<const uint2 *>(g.ubuf + o);
-          const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
-          float dg[4], du[4], hh[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t gb = (j & 1) ? (gw[j >> 1] & 0xFFFF0000u) : (gw[j >> 1] << 16);
-            const uint32_t ub = (j & 1) ? (uw[j >> 1] & 0xFFFF0000u) : (uw[j >> 1] << 16);
-            const float gg = __uint_as_float(gb), uu = __uint_as_float(ub);
-            const float sg = 1.0f / (1.0f + expf(-gg));
-            const float v = acc[a2][nb][gi * 4 + j];
-            hh[j] = gg * sg * uu;
-            dsum += v * hh[j];
-            const float dh = gt * v;
-            dg[j] = dh * uu * sg * (1.0f + gg * (1.0f - sg));
-            du[j] = dh * gg * sg;
-          }
-          store4<bf16_t>(g.gbuf + o, dg[0], dg[1], dg[2], dg[3]);
-          store4<bf16_t>(g.ubuf + o, du[0], du[1], du[2], du[3]);
-          store4<bf16_t>(g.hbuf + o, hh[0], hh[1], hh[2], hh[3]);
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t gb = (j & 1) ? (gw[j >> 1] & 0xFFFF0000u) : (gw[j >> 1] << 16);
+          const uint32_t ub = (j & 1) ? (uw[j >> 1] & 0xFFFF0000u) : (uw[j >> 1] << 16);
+          const float gg = __uint_as_float(gb), uu = __uint_as_float(ub);
+          const float sg = 1.0f / (1.0f + expf(-gg));
+          const float v = acc[a2][nb][gi * 4 + j];
+          hh[j] = gg * sg * uu;
+          dsum += v * hh[j];  // zero for rows past the tile (G, U read as zeros)
+          const float dh = gt[cur] * v;
+          dg[j] = dh * uu * sg * (1.0f + gg * (1.0f - sg));
+          du[j] = dh * gg * sg;
         }
+        auto pack = [](const float (&f)[4]) {
+          return make_uint2(
+              static_cast<uint32_t>(f32_to_bf16(f[0])) | (static_cast<uint32_t>(f32_to_bf16(f[1])) << 16),
+              static_cast<uint32_t>(f32_to_bf16(f[2])) | (static_cast<uint32_t>(f32_to_bf16(f[3])) << 16));
+        };
+        const int o = static_cast<int>(eoff(nb, a2, gi));
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const uint2 pg = pack(dg), pu = pack(du), ph = pack(hh);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pg.x, pg.y}, rg, o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pu.x, pu.y}, ru, o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{ph.x, ph.y}, rh, o, 0, 0);
+      }
       dsum += __shfl_xor(dsum, 32, kWave);
       if (h == 0) s_part[nb * 32 + r] = dsum;
     }
@@ -455,28 +486,36 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs &g, int e, int r0, in
     mn_load(w[pos], a, ks);
   });
   // ---- epilogue: C[m, n] += acc (fp32 read-modify-write; every element of
-  // the output has one owner per launch) ----
-  float *cbase = g.c + static_cast<int64_t>(e) * g.c_stride;
-#pragma unroll
-  for (int nb = 0; nb < NBR; ++nb) {
+  // the output has one owner per launch).  All of the tile's old values are
+  // loaded before the first store, so their latencies overlap (stores and
+  // loads to one array would otherwise be kept in program order). ----
+  // Buffer loads and stores with out-of-range offsets for the tile's edges:
+  // no branches, so nothing splits the batch.
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(g.c + static_cast<int64_t>(e) * g.c_stride, static_cast<uint32_t>(g.M) * g.Ncols * 4);
+  auto coff = [&](int nb, int a2, int i) -> uint32_t {
     const int n = n0 + nb * 32 + r;
-    if (n >= g.Ncols) continue;
-    float old[32];
+    const int m = m_base + a2 * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+    return (m < g.M && n < g.Ncols) ? static_cast<uint32_t>(m * g.Ncols + n) * 4u : kOOB;
+  };
+  float old[NBR][32];
+#pragma unroll
+  for (int nb = 0; nb < NBR; ++nb)
 #pragma unroll
     for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m_base + a2 * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-        old[a2 * 16 + i] = m < g.M ? cbase[static_cast<int64_t>(m) * g.Ncols + n] : 0.0f;
-      }
+      for (int i = 0; i < 16; ++i)
+        old[nb][a2 * 16 + i] = __uint_as_float(static_cast<uint32_t>(
+            __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(coff(nb, a2, i)), 0, 0)));
+#pragma unroll
+  for (int nb = 0; nb < NBR; ++nb)
 #pragma unroll
     for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m_base + a2 * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-        if (m < g.M) cbase[static_cast<int64_t>(m) * g.Ncols + n] = old[a2 * 16 + i] + acc[a2][nb][i];
-      }
-  }
+      for (int i = 0; i < 16; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __float_as_uint(old[nb][a2 * 16 + i] + acc[a2][nb][i]), rc,
+            static_cast<int>(coff(nb, a2, i)), 0, 0);
 }
 
 template <int NB>

@@ -198,9 +198,11 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
 #pragma unroll
   for (int i = 0; i < NBR; ++i) {
     const int tr = brow + 32 * i;
-    uint32_t row = 0;
-    if (tr < mcount) row = MODE == MODE8_GATE_UP ? static_cast<uint32_t>(g.tok[m0 + tr]) : tr;
-    st.vob[i] = tr < mcount ? row * K + bp * 16 : kOOB;
+    // clamped index load whose value is always used (kOOB added for rows
+    // past the chunk), so the NBR loads issue together
+    const uint32_t row = MODE == MODE8_GATE_UP ? static_cast<uint32_t>(g.tok[m0 + min(tr, mcount - 1)])
+                                               : static_cast<uint32_t>(tr);
+    st.vob[i] = row * K + bp * 16 + (tr < mcount ? 0u : kOOB);
   }
 
   // Exponents into LDS, once per tile.  s_sa: two rows of nkb bytes, the

@@ -321,8 +321,11 @@ static bool bwd_dims_ok(const moe_zc_dims *dm, int *status) {
   // matrix are bounded by dims_ok)
   const int64_t E = static_cast<int64_t>(dm->N) + dm->Z;
   const int64_t lim = int64_t(1) << 31;
-  if (E * dm->d * 2 >= lim || dm->T * ((E + 7) / 8 * 8) * 2 >= lim ||
-      (dm->N > 0 && dm->T * dm->I * 2 >= lim)) {
+  // (the fp32 weight gradients of one matrix too: the wgrad epilogue reads
+  // and writes them through buffer descriptors)
+  if (E * dm->d * 4 >= lim || dm->T * ((E + 7) / 8 * 8) * 2 >= lim ||
+      (dm->N > 0 && (dm->T * dm->I * 2 >= lim ||
+                     static_cast<int64_t>(dm->d) * dm->I * 4 >= lim))) {
     *status = MOE_ZC_EINVAL;
     return false;
   }
