@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time moe_zc_backward (the block's backward with fp32 weight-gradient "
                          "accumulation); a separate line, not the forward headline")
+    ap.add_argument("--scmoe", action="store_true",
+                    help="time the shortcut-connected layer schedule: the MoE block and the "
+                         "dense SwiGLU FFN (width 12288) serial, on two streams, and with the "
+                         "MoE in two token chunks; a separate line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -299,6 +303,85 @@ def backward_bench(args, cfg, inp, dev):
     print(json.dumps(res), flush=True)
 
 
+def scmoe_bench(args, cfg, inp, dev):
+    import torch
+
+    import synth
+    import zero_computation_expert_amd as moe
+
+    Id = synth.DENSE_WIDTH
+    dn = synth.device_dense(cfg, Id, dev)
+    s0 = torch.cuda.current_stream(dev)
+    s1 = torch.cuda.Stream(device=dev)
+    a1, b1 = moe.scmoe_workspace_bytes(cfg.T, cfg.d, cfg.I, cfg.N, cfg.Z, cfg.k, Id, 1)
+    ws_moe = torch.empty(a1, dtype=torch.uint8, device=dev)
+    ws_dense = torch.empty(b1, dtype=torch.uint8, device=dev)
+    out_moe = torch.empty_like(inp["x"])
+    out_dense = torch.empty_like(dn["x_dense"])
+    counts = torch.empty((2, cfg.E), dtype=torch.int32, device=dev)
+
+    def layer(nchunks, two):
+        moe.scmoe_forward(inp["x"], inp["W_router"], inp["bias"], inp["W_gate"], inp["W_up"],
+                          inp["W_down"], dn["x_dense"], dn["W1"], dn["W3"], dn["W2"], cfg.N,
+                          cfg.Z, cfg.k, nchunks, s0, s1 if two else s0, out_moe=out_moe,
+                          out_dense=out_dense, counts=counts[:nchunks], ws_moe=ws_moe,
+                          ws_dense=ws_dense)
+
+    def moe_only():
+        moe.forward(inp["x"], inp["W_router"], inp["bias"], inp["W_gate"], inp["W_up"],
+                    inp["W_down"], cfg.N, cfg.Z, cfg.k, out=out_moe, counts=counts[0],
+                    workspace=ws_moe, want_routing=False)
+
+    def dense_only():
+        moe.dense_ffn(dn["x_dense"], dn["W1"], dn["W3"], dn["W2"], out=out_dense,
+                      workspace=ws_dense)
+
+    def timed(fn):
+        # each step starts both streams together and joins them at its end
+        for _ in range(args.warmup):
+            s1.wait_stream(s0)
+            fn()
+            s0.wait_stream(s1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s0)
+        for _ in range(args.steps):
+            s1.wait_stream(s0)
+            fn()
+            s0.wait_stream(s1)
+        e1.record(s0)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms = {"moe_only": timed(moe_only), "dense_only": timed(dense_only),
+          "serial": timed(lambda: layer(1, False)), "two_streams": timed(lambda: layer(1, True)),
+          "two_chunks_serial": timed(lambda: layer(2, False)),
+          "two_chunks_two_streams": timed(lambda: layer(2, True))}
+    print("[bench] scmoe " + " ".join(f"{k}={v:.3f}" for k, v in ms.items()), file=sys.stderr,
+          flush=True)
+    best = min(("two_streams", "two_chunks_two_streams"), key=lambda k: ms[k])
+    dense_flops = 6 * cfg.T * cfg.d * Id
+    dense_tf = dense_flops / (ms["dense_only"] / 1e3) / 1e12
+    res = {
+        "metric": "shortcut-connected layer (MoE block + dense SwiGLU FFN) tokens/s at 1 MI355X",
+        "value": round(cfg.T / (ms[best] / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms[best], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Philox4x64 normals; random-init weights)",
+        "config": {"workload": f"{cfg.name} MoE (T={cfg.T} d={cfg.d} I={cfg.I} N={cfg.N} "
+                               f"Z={cfg.Z} k={cfg.k}) + dense SwiGLU FFN width {Id}, bf16",
+                   "schedule": best},
+        "schedules_ms": {k: round(v, 4) for k, v in ms.items()},
+        "overlap_saving": round(1.0 - ms[best] / ms["serial"], 4),
+        "roofline": {"bound": "mfma", "kernel": "dense FFN on gemm_kernel (gate/up + down)",
+                     "achieved": round(dense_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dense_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_call": dense_flops,
+                     "avg_call_ms": round(ms["dense_only"], 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -328,6 +411,9 @@ def main():
     dt_code = moe.BF16 if cfg.dtype == "bf16" else moe.F32
     if args.backward:
         backward_bench(args, cfg, inp, dev)
+        return
+    if args.scmoe:
+        scmoe_bench(args, cfg, inp, dev)
         return
     if args.fp8:
         # quantize the expert weights once, untimed ([128,128] blocks), and

@@ -189,6 +189,51 @@ void moe_zc_timer_reset(moe_zc_timer *timer);
 void moe_zc_timer_destroy(moe_zc_timer *timer);
 
 /* ------------------------------------------------------------------------
+ * Dense SwiGLU FFN and the two-stream ScMoE schedule.
+ *
+ * LongCat-Flash technical-report summary page, section 2 "architecture",
+ * shortcut-connected MoE (ScMoE): a shortcut from the layer's first
+ * attention output feeds the MoE block, so the MoE runs alongside the dense
+ * FFN block instead of after it; section 5 "training infrastructure": the
+ * MoE layer is split into two chunks along the token dimension, which
+ * overlap with the dense FFN and with each other.  The model-configuration
+ * paragraph gives the dense FFN path an intermediate width of 12288.
+ *
+ * moe_zc_dense_ffn: out[t] = W2 (silu(W1 x[t]) * (W3 x[t])), bfloat16,
+ *   x [T, d], W1 and W3 [I_dense, d], W2 [d, I_dense], out [T, d] (must not
+ *   overlap x); d and I_dense multiples of 8; workspace of
+ *   moe_zc_dense_workspace_bytes(T, d, I_dense) bytes, 256-byte aligned.
+ *   It runs on the expert GEMM kernels as one expert that every token uses.
+ *
+ * moe_zc_scmoe_forward: enqueues the MoE block over x_moe on stream_moe, in
+ *   nchunks (1 or 2) consecutive token chunks of ceil(T / nchunks) rows, and
+ *   the dense FFN over x_dense on stream_dense; the two inputs are
+ *   independent (the shortcut).  Each MoE chunk is moe_zc_forward on its
+ *   rows (routing is per token; the chunks share ws_moe, so they run in
+ *   order on stream_moe); counts is [nchunks, N+Z], chunk c's counts in row
+ *   c; topk_idx / topk_gate [T, k] nullable.  Passing one stream for both is
+ *   the serial schedule.  The caller joins the two streams.  Workspace sizes
+ *   from moe_zc_scmoe_workspace_bytes.  bfloat16 only.  Everything is
+ *   validated before anything is enqueued.
+ * ------------------------------------------------------------------------ */
+size_t moe_zc_dense_workspace_bytes(int64_t T, int32_t d, int32_t I_dense);
+
+int moe_zc_dense_ffn(int64_t T, int32_t d, int32_t I_dense, const void *x, const void *W1,
+                     const void *W3, const void *W2, void *out, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+int moe_zc_scmoe_workspace_bytes(const moe_zc_dims *dims, int32_t I_dense, int32_t nchunks,
+                                 size_t *ws_moe, size_t *ws_dense);
+
+int moe_zc_scmoe_forward(const moe_zc_dims *dims, int32_t I_dense, int32_t nchunks,
+                         const void *x_moe, const void *W_router, const float *bias,
+                         const void *W_gate, const void *W_up, const void *W_down,
+                         const void *x_dense, const void *W1, const void *W3, const void *W2,
+                         void *out_moe, void *out_dense, int32_t *counts, int32_t *topk_idx,
+                         float *topk_gate, void *ws_moe, size_t ws_moe_bytes, void *ws_dense,
+                         size_t ws_dense_bytes, void *stream_moe, void *stream_dense);
+
+/* ------------------------------------------------------------------------
  * Backward of the block (training).
  *
  * LongCat-Flash technical-report summary page, section 5 "training

@@ -76,6 +76,7 @@ def _load():
         lib.oracle_token_backward.argtypes = [i32, i32, i32, i32, i32, vp, i32] + [vp] * 13
         lib.oracle_backward.argtypes = [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                         vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_dense_ffn.argtypes = [i64, i32, i32, vp, i32, vp, vp, vp, vp]
         lib.oracle_expert_wgrad_row.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, i32,
                                                 vp, vp, vp]
         _lib = lib
@@ -385,3 +386,14 @@ def expert_wgrad_row(x_rows, dt: str, dout_rows, gates, wg, wu, wd, r: int) -> d
                                     _ptr(wg), _ptr(wu), _ptr(wd), r, _ptr(dwg), _ptr(dwu),
                                     _ptr(dwd))
     return {"dw_gate_row": dwg, "dw_up_row": dwu, "dw_down_col": dwd}
+
+
+def dense_ffn(x, w1, w3, w2, dt: str) -> np.ndarray:
+    """The dense SwiGLU FFN: out [T, d] = W2 (silu(W1 x) * (W3 x)), fp32."""
+    x = _storage(x, dt)
+    T, d = x.shape
+    w1, w3, w2 = (_storage(a, dt) for a in (w1, w3, w2))
+    I = w1.shape[0]
+    out = np.empty((T, d), dtype=np.float32)
+    _load().oracle_dense_ffn(T, d, I, _ptr(x), _DT[dt], _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out))
+    return out

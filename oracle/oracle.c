@@ -695,3 +695,25 @@ void oracle_expert_wgrad_row(int d, int I, int n, const void *x_rows, int dt,
     }
   }
 }
+
+/* The dense FFN path of the layer ([LCF] section 2, shortcut-connected MoE
+ * and the model-configuration paragraph: a dense SwiGLU FFN block beside the
+ * MoE, intermediate width 12288 at the production shape):
+ * out[t] = W2 (silu(W1 x[t]) * (W3 x[t])), W1 / W3 [I, d], W2 [d, I]. */
+void oracle_dense_ffn(int64_t T, int d, int I, const void *x, int dt, const void *w1,
+                      const void *w3, const void *w2, float *out) {
+  const size_t es = dt == ORC_F32 ? 4 : 2;
+#pragma omp parallel
+  {
+    float *xf = (float *)malloc(sizeof(float) * (size_t)d);
+    float *h = (float *)malloc(sizeof(float) * (size_t)(I > 0 ? I : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      const void *xr = (const char *)x + (size_t)t * (size_t)d * es;
+      for (int c = 0; c < d; ++c) xf[c] = orc_ld(xr, c, dt);
+      orc_expert(d, I, xf, w1, w3, w2, dt, h, out + t * (int64_t)d);
+    }
+    free(xf);
+    free(h);
+  }
+}

@@ -37,6 +37,10 @@ _GOLDEN = os.path.join(os.path.dirname(_HERE), "tests", "golden")
 
 TID_X, TID_WR, TID_BIAS, TID_WG, TID_WU, TID_WD = 0, 1, 2, 3, 4, 5
 TID_DOUT = 6  # output gradient of the backward, N(0, 1) in the inputs' dtype
+# the dense FFN block beside the MoE: its input x_dense ~ N(0, 1) and its
+# SwiGLU matrices W1, W3 [I_dense, d], W2 [d, I_dense] ~ N(0, 1/d)
+TID_XD, TID_D1, TID_D3, TID_D2 = 7, 8, 9, 10
+DENSE_WIDTH = 12288  # the dense FFN path's intermediate width at the production shape
 
 
 @dataclass(frozen=True)
@@ -284,3 +288,21 @@ def device_inputs(cfg: Config, device="cuda:0") -> dict:
 def device_dout(cfg: Config, device="cuda:0"):
     """The output gradient of host_dout, generated in device memory."""
     return device_normal((cfg.T, cfg.d), 0, cfg.seed, TID_DOUT, 1.0, cfg.dtype, device)
+
+
+def host_dense(cfg: Config, I_dense: int) -> dict:
+    """x_dense [T, d] and the dense FFN matrices, in the inputs' dtype."""
+    sw = sigma_weights(cfg)
+    return {"x_dense": host_normal((cfg.T, cfg.d), 0, cfg.seed, TID_XD, 1.0, cfg.dtype),
+            "W1": host_normal((I_dense, cfg.d), 0, cfg.seed, TID_D1, sw, cfg.dtype),
+            "W3": host_normal((I_dense, cfg.d), 0, cfg.seed, TID_D3, sw, cfg.dtype),
+            "W2": host_normal((cfg.d, I_dense), 0, cfg.seed, TID_D2, sw, cfg.dtype)}
+
+
+def device_dense(cfg: Config, I_dense: int, device="cuda:0") -> dict:
+    """The tensors of host_dense, generated in device memory."""
+    sw = sigma_weights(cfg)
+    return {"x_dense": device_normal((cfg.T, cfg.d), 0, cfg.seed, TID_XD, 1.0, cfg.dtype, device),
+            "W1": device_normal((I_dense, cfg.d), 0, cfg.seed, TID_D1, sw, cfg.dtype, device),
+            "W3": device_normal((I_dense, cfg.d), 0, cfg.seed, TID_D3, sw, cfg.dtype, device),
+            "W2": device_normal((cfg.d, I_dense), 0, cfg.seed, TID_D2, sw, cfg.dtype, device)}

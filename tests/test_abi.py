@@ -245,3 +245,54 @@ def test_backward_rejects_dims():
     assert moe.lib().moe_zc_backward_workspace_bytes(ctypes.byref(D(dtype=moe.F32))) == 0
     big = moe.lib().moe_zc_backward_workspace_bytes(ctypes.byref(D(T=4096)))
     assert big > moe.lib().moe_zc_backward_workspace_bytes(ctypes.byref(D(T=64))) > 0
+
+
+def test_dense_ffn_rejects():
+    lib = moe.lib()
+    need = lib.moe_zc_dense_workspace_bytes(64, 128, 256)
+    assert need > 0 and lib.moe_zc_dense_workspace_bytes(64, 100, 256) == 0
+
+    def dense(T=64, d=128, Id=256, x=A, w1=2 * A, w3=3 * A, w2=4 * A, out=5 * A, ws=16 * A,
+              nb=None):
+        st = lib.moe_zc_dense_ffn(T, d, Id, x, w1, w3, w2, out, ws, need if nb is None else nb,
+                                  None)
+        assert st != 0, "a test call passed validation: it would have launched work"
+        return st
+
+    assert dense(d=100) == EALIGN
+    assert dense(Id=60) == EALIGN
+    assert dense(x=None) == EINVAL
+    assert dense(out=A + 32) == EINVAL   # out overlaps x
+    assert dense(w2=4 * A + 4) == EALIGN
+    assert dense(nb=need - 1) == ENOSPC
+    assert dense(ws=16 * A + 16) == EALIGN
+
+
+def test_scmoe_rejects():
+    lib = moe.lib()
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.moe_zc_scmoe_workspace_bytes(ctypes.byref(D()), 256, 3, ctypes.byref(a),
+                                            ctypes.byref(b)) == EINVAL
+    assert lib.moe_zc_scmoe_workspace_bytes(ctypes.byref(D(dtype=moe.F32)), 256, 2,
+                                            ctypes.byref(a), ctypes.byref(b)) == EDTYPE
+    assert lib.moe_zc_scmoe_workspace_bytes(ctypes.byref(D()), 256, 2, ctypes.byref(a),
+                                            ctypes.byref(b)) == 0
+    one, two = a.value, ctypes.c_size_t()
+    assert lib.moe_zc_scmoe_workspace_bytes(ctypes.byref(D()), 256, 1, ctypes.byref(two),
+                                            ctypes.byref(b)) == 0
+    assert two.value > one  # two chunks need a workspace of half the tokens
+
+    def sc(nchunks=2, counts=8 * A, ws_moe_bytes=None, x_dense=20 * A, out_dense=21 * A):
+        st = lib.moe_zc_scmoe_forward(ctypes.byref(D()), 256, nchunks, A, 2 * A, 3 * A, 4 * A,
+                                      5 * A, 6 * A, x_dense, 22 * A, 23 * A, 24 * A, 7 * A,
+                                      out_dense, counts, None, None, 16 * A,
+                                      one if ws_moe_bytes is None else ws_moe_bytes, 32 * A,
+                                      b.value, None, None)
+        assert st != 0, "a test call passed validation: it would have launched work"
+        return st
+
+    assert sc(nchunks=0) == EINVAL
+    assert sc(counts=None) == EINVAL
+    assert sc(ws_moe_bytes=one - 1) == ENOSPC
+    assert sc(out_dense=7 * A + 64) == EINVAL    # overlaps out_moe
+    assert sc(x_dense=None) == EINVAL

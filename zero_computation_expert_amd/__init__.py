@@ -26,7 +26,8 @@ EXPORTS = ("moe_zc_workspace_bytes", "moe_zc_forward", "moe_zc_status_string",
            "moe_zc_timer_create", "moe_zc_forward_timed", "moe_zc_timer_read",
            "moe_zc_timer_reset", "moe_zc_timer_destroy", "moe_zc_bias_update",
            "moe_zc_quantize_fp8", "moe_zc_workspace_bytes_fp8", "moe_zc_forward_fp8",
-           "moe_zc_backward_workspace_bytes", "moe_zc_backward")
+           "moe_zc_backward_workspace_bytes", "moe_zc_backward", "moe_zc_dense_workspace_bytes",
+           "moe_zc_dense_ffn", "moe_zc_scmoe_workspace_bytes", "moe_zc_scmoe_forward")
 
 
 class MoeZcError(RuntimeError):
@@ -83,6 +84,17 @@ def lib():
         L.moe_zc_backward_workspace_bytes.argtypes = [dims_p]
         L.moe_zc_backward.restype = ctypes.c_int
         L.moe_zc_backward.argtypes = [dims_p] + [vp] * 14 + [sz, vp, vp]
+        L.moe_zc_dense_workspace_bytes.restype = sz
+        L.moe_zc_dense_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+        L.moe_zc_dense_ffn.restype = ctypes.c_int
+        L.moe_zc_dense_ffn.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [vp] * 6 \
+            + [sz, vp]
+        L.moe_zc_scmoe_workspace_bytes.restype = ctypes.c_int
+        L.moe_zc_scmoe_workspace_bytes.argtypes = [dims_p, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.moe_zc_scmoe_forward.restype = ctypes.c_int
+        L.moe_zc_scmoe_forward.argtypes = [dims_p, ctypes.c_int32, ctypes.c_int32] + [vp] * 15 \
+            + [vp, sz, vp, sz, vp, vp]
         f32 = ctypes.c_float
         L.moe_zc_bias_update.restype = ctypes.c_int
         L.moe_zc_bias_update.argtypes = [ctypes.c_int32, ctypes.c_int64, vp, vp, vp, vp, f32, f32,
@@ -326,3 +338,76 @@ def backward(x, W_router, W_gate, W_up, W_down, topk_idx, topk_gate, dout, N: in
         _ptr(dW_up), _ptr(dW_down), _ptr(workspace), workspace.numel() * workspace.element_size(),
         stream, timer.handle if timer is not None else None))
     return dx, dW_router, dW_gate, dW_up, dW_down
+
+
+# ---------------------------------------------------------------------------
+# Dense SwiGLU FFN and the two-stream ScMoE schedule
+# ---------------------------------------------------------------------------
+
+def dense_workspace_bytes(T, d, I_dense) -> int:
+    return int(lib().moe_zc_dense_workspace_bytes(int(T), int(d), int(I_dense)))
+
+
+def dense_ffn(x, W1, W3, W2, *, out=None, workspace=None, stream=None):
+    """moe_zc_dense_ffn on bfloat16 device tensors: x [T, d], W1 / W3
+    [I_dense, d], W2 [d, I_dense]; returns out [T, d]."""
+    import torch
+
+    T, d = x.shape
+    Id = W1.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(max(dense_workspace_bytes(T, d, Id), 1), dtype=torch.uint8,
+                                device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    _check(lib().moe_zc_dense_ffn(int(T), int(d), int(Id), _ptr(x), _ptr(W1), _ptr(W3), _ptr(W2),
+                                  _ptr(out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), stream))
+    return out
+
+
+def scmoe_workspace_bytes(T, d, I, N, Z, k, I_dense, nchunks):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().moe_zc_scmoe_workspace_bytes(ctypes.byref(make_dims(T, d, I, N, Z, k, BF16)),
+                                              int(I_dense), int(nchunks), ctypes.byref(a),
+                                              ctypes.byref(b)))
+    return a.value, b.value
+
+
+def scmoe_forward(x_moe, W_router, bias, W_gate, W_up, W_down, x_dense, W1, W3, W2, N: int,
+                  Z: int, k: int, nchunks: int, stream_moe, stream_dense, *, out_moe=None,
+                  out_dense=None, counts=None, topk_idx=None, topk_gate=None, ws_moe=None,
+                  ws_dense=None):
+    """moe_zc_scmoe_forward: the MoE over x_moe (nchunks token chunks) on
+    stream_moe and the dense FFN over x_dense on stream_dense (torch streams
+    or raw handles).  Returns (out_moe, out_dense, counts [nchunks, N+Z],
+    topk_idx, topk_gate)."""
+    import torch
+
+    T, d = x_moe.shape
+    I = W_gate.shape[1] if (W_gate is not None and N > 0) else 0
+    Id = W1.shape[0]
+    dev = x_moe.device
+    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x_moe))
+    if out_moe is None:
+        out_moe = torch.empty_like(x_moe)
+    if out_dense is None:
+        out_dense = torch.empty_like(x_dense)
+    if counts is None:
+        counts = torch.empty((nchunks, N + Z), dtype=torch.int32, device=dev)
+    if ws_moe is None or ws_dense is None:
+        a, b = scmoe_workspace_bytes(T, d, I, N, Z, k, Id, nchunks)
+        if ws_moe is None:
+            ws_moe = torch.empty(max(a, 1), dtype=torch.uint8, device=dev)
+        if ws_dense is None:
+            ws_dense = torch.empty(max(b, 1), dtype=torch.uint8, device=dev)
+    h = lambda s: s.cuda_stream if hasattr(s, "cuda_stream") else s  # noqa: E731
+    _check(lib().moe_zc_scmoe_forward(
+        ctypes.byref(dims), int(Id), int(nchunks), _ptr(x_moe), _ptr(W_router), _ptr(bias),
+        _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(x_dense), _ptr(W1), _ptr(W3), _ptr(W2),
+        _ptr(out_moe), _ptr(out_dense), _ptr(counts), _ptr(topk_idx), _ptr(topk_gate),
+        _ptr(ws_moe), ws_moe.numel(), _ptr(ws_dense), ws_dense.numel(), h(stream_moe),
+        h(stream_dense)))
+    return out_moe, out_dense, counts, topk_idx, topk_gate

@@ -142,7 +142,8 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
                         const float *bias, const void *w_gate, const void *w_up,
                         const void *w_down, void *out, int32_t *counts, int32_t *topk_idx,
                         float *topk_gate, void *workspace, size_t workspace_bytes, void *stream,
-                        moe_zc_timer *timer, const Fp8Scales *f8 = nullptr) {
+                        moe_zc_timer *timer, const Fp8Scales *f8 = nullptr,
+                        bool launch = true) {
   int st;
   if (!(f8 ? fp8_dims_ok(dm, &st) : dims_ok(dm, &st))) return st;
   if (f8 && dm->T > 0 && dm->N > 0 && (!f8->gate || !f8->up || !f8->down)) return MOE_ZC_EINVAL;
@@ -167,6 +168,7 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
     if (!aligned(workspace, 256)) return MOE_ZC_EALIGN;
   }
   if (timer && timer->ncalls >= timer->max_calls) return MOE_ZC_ENOSPC;
+  if (!launch) return MOE_ZC_OK;  // validation only
 
   Plan p = {};
   p.T = T;
@@ -431,6 +433,76 @@ static int backward_impl(const moe_zc_dims *dm, const void *x, const void *w_rou
   return MOE_ZC_OK;
 }
 
+// ---- dense SwiGLU FFN and the two-stream ScMoE schedule --------------------
+// The dense FFN y = W2 (silu(W1 x) * (W3 x)) runs on the expert GEMM kernels
+// as a single expert that every token uses (identity permutation).
+static bool dense_dims_ok(int64_t T, int d, int Id) {
+  const int64_t lim = int64_t(1) << 31;
+  return T >= 0 && d >= 8 && Id >= 8 && d % 8 == 0 && Id % 8 == 0 && T * d * 2 < lim &&
+         static_cast<int64_t>(Id) * d * 2 < lim && T < lim;
+}
+
+static size_t layout_dense(int64_t T, int Id, char *base, Plan *p) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *ptr = base ? base + off : nullptr;
+    off = align_up(off + bytes);
+    return ptr;
+  };
+  char *tok = take(static_cast<size_t>(T) * 4);
+  char *offs = take(8);
+  char *chunk_off = take(8);
+  char *meta = take(64);
+  char *h = take(static_cast<size_t>(T) * Id * 2);
+  if (p) {
+    p->tok = reinterpret_cast<int32_t *>(tok);
+    p->offs = reinterpret_cast<int32_t *>(offs);
+    p->chunk_off = reinterpret_cast<int32_t *>(chunk_off);
+    p->meta = reinterpret_cast<int32_t *>(meta);
+    p->h = h;
+  }
+  return off;
+}
+
+static int dense_impl(int64_t T, int d, int Id, const void *x, const void *w1, const void *w3,
+                      const void *w2, void *out, void *workspace, size_t workspace_bytes,
+                      hipStream_t s, bool launch) {
+  if (!dense_dims_ok(T, d, Id)) return (d % 8 || Id % 8) ? MOE_ZC_EALIGN : MOE_ZC_EINVAL;
+  if (T == 0) return MOE_ZC_OK;
+  const size_t xbytes = static_cast<size_t>(T) * d * 2;
+  if (!x || !w1 || !w3 || !w2 || !out) return MOE_ZC_EINVAL;
+  if (overlap(x, xbytes, out, xbytes)) return MOE_ZC_EINVAL;
+  const void *p16[] = {x, w1, w3, w2, out};
+  for (const void *ptr : p16)
+    if (!aligned(ptr, 16)) return MOE_ZC_EALIGN;
+  if (workspace == nullptr || workspace_bytes < layout_dense(T, Id, nullptr, nullptr))
+    return MOE_ZC_ENOSPC;
+  if (!aligned(workspace, 256)) return MOE_ZC_EALIGN;
+  if (!launch) return MOE_ZC_OK;
+  Plan p = {};
+  p.T = T;
+  p.d = d;
+  p.I = Id;
+  p.N = 1;
+  p.E = 1;
+  p.k = 1;
+  p.dtype = MOE_ZC_BF16;
+  p.pmax = T;
+  p.nbmax = T >= 96 ? 5 : (T >= 24 ? 4 : 1);
+  p.x = x;
+  p.w_gate = w1;
+  p.w_up = w3;
+  p.w_down = w2;
+  layout_dense(T, Id, static_cast<char *>(workspace), &p);
+  p.y = out;  // the identity permutation writes token rows in place
+  if (launch_dense_route(p, s) != hipSuccess || launch_gate_up(p, s) != hipSuccess ||
+      launch_down(p, s) != hipSuccess)
+    return MOE_ZC_EHIP;
+  return MOE_ZC_OK;
+}
+
+static int64_t chunk_rows(int64_t T, int nchunks) { return (T + nchunks - 1) / nchunks; }
+
 extern "C" {
 
 size_t moe_zc_workspace_bytes_fp8(const moe_zc_dims *dims) {
@@ -488,6 +560,78 @@ int moe_zc_backward(const moe_zc_dims *dims, const void *x, const void *W_router
   return backward_impl(dims, x, W_router, W_gate, W_up, W_down, topk_idx, topk_gate, dout, dx,
                        dW_router, dW_gate, dW_up, dW_down, workspace, workspace_bytes, stream,
                        timer);
+}
+
+size_t moe_zc_dense_workspace_bytes(int64_t T, int32_t d, int32_t I_dense) {
+  if (!dense_dims_ok(T, d, I_dense)) return 0;
+  return layout_dense(T, I_dense, nullptr, nullptr);
+}
+
+int moe_zc_dense_ffn(int64_t T, int32_t d, int32_t I_dense, const void *x, const void *W1,
+                     const void *W3, const void *W2, void *out, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  return dense_impl(T, d, I_dense, x, W1, W3, W2, out, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream), true);
+}
+
+int moe_zc_scmoe_workspace_bytes(const moe_zc_dims *dims, int32_t I_dense, int32_t nchunks,
+                                 size_t *ws_moe, size_t *ws_dense) {
+  int st;
+  if (!ws_moe || !ws_dense || nchunks < 1 || nchunks > 2) return MOE_ZC_EINVAL;
+  if (!dims_ok(dims, &st)) return st;
+  if (dims->dtype != MOE_ZC_BF16) return MOE_ZC_EDTYPE;
+  if (!dense_dims_ok(dims->T, dims->d, I_dense)) return MOE_ZC_EINVAL;
+  moe_zc_dims c = *dims;
+  c.T = chunk_rows(dims->T, nchunks);
+  *ws_moe = layout(&c, nullptr, nullptr);
+  *ws_dense = layout_dense(dims->T, I_dense, nullptr, nullptr);
+  return MOE_ZC_OK;
+}
+
+int moe_zc_scmoe_forward(const moe_zc_dims *dims, int32_t I_dense, int32_t nchunks,
+                         const void *x_moe, const void *W_router, const float *bias,
+                         const void *W_gate, const void *W_up, const void *W_down,
+                         const void *x_dense, const void *W1, const void *W3, const void *W2,
+                         void *out_moe, void *out_dense, int32_t *counts, int32_t *topk_idx,
+                         float *topk_gate, void *ws_moe, size_t ws_moe_bytes, void *ws_dense,
+                         size_t ws_dense_bytes, void *stream_moe, void *stream_dense) {
+  size_t need_moe = 0, need_dense = 0;
+  const int st0 = moe_zc_scmoe_workspace_bytes(dims, I_dense, nchunks, &need_moe, &need_dense);
+  if (st0 != MOE_ZC_OK) return st0;
+  (void)need_dense;  // dense_impl checks its own workspace
+  const int64_t T = dims->T;
+  // validate everything before enqueueing anything: the dense FFN, then
+  // each chunk's forward with launches suppressed
+  int st = dense_impl(T, dims->d, I_dense, x_dense, W1, W3, W2, out_dense, ws_dense,
+                      ws_dense_bytes, static_cast<hipStream_t>(stream_dense), false);
+  if (st != MOE_ZC_OK) return st;
+  if (counts == nullptr) return MOE_ZC_EINVAL;
+  if (T > 0 && ws_moe_bytes < need_moe) return MOE_ZC_ENOSPC;
+  const size_t xbytes = static_cast<size_t>(T) * dims->d * 2;
+  if (overlap(out_moe, xbytes, out_dense, xbytes) || overlap(out_moe, xbytes, x_dense, xbytes) ||
+      overlap(out_dense, xbytes, x_moe, xbytes))
+    return MOE_ZC_EINVAL;
+  const int64_t rows = chunk_rows(T, nchunks);
+  const int E = dims->N + dims->Z;
+  for (int pass = 0; pass < 2; ++pass) {
+    // MoE chunks in token order on stream_moe (a chunk past T has no rows:
+    // its counts are zeroed)
+    for (int c = 0; c < nchunks; ++c) {
+      const int64_t t0 = std::min<int64_t>(c * rows, T);
+      moe_zc_dims cd = *dims;
+      cd.T = std::min<int64_t>(rows, T - t0);
+      const size_t ro = static_cast<size_t>(t0) * dims->d * 2;
+      st = forward_impl(&cd, static_cast<const char *>(x_moe) + ro, W_router, bias, W_gate, W_up,
+                        W_down, static_cast<char *>(out_moe) + ro, counts + static_cast<size_t>(c) * E,
+                        topk_idx ? topk_idx + t0 * dims->k : nullptr,
+                        topk_gate ? topk_gate + t0 * dims->k : nullptr, ws_moe, ws_moe_bytes,
+                        stream_moe, nullptr, nullptr, pass == 1);
+      if (st != MOE_ZC_OK) return st;
+    }
+  }
+  // then the dense FFN, whole, on stream_dense
+  return dense_impl(T, dims->d, I_dense, x_dense, W1, W3, W2, out_dense, ws_dense, ws_dense_bytes,
+                    static_cast<hipStream_t>(stream_dense), true);
 }
 
 const char *moe_zc_status_string(int status) {

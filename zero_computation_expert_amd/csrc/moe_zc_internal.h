@@ -132,6 +132,7 @@ hipError_t launch_zero_counts(const Plan &p, hipStream_t s);
 hipError_t launch_quant_x(const Plan &p, hipStream_t s);
 hipError_t launch_gate_up8(const Plan &p, hipStream_t s);
 hipError_t launch_down8(const Plan &p, hipStream_t s);
+hipError_t launch_dense_route(const Plan &p, hipStream_t s);  // dense FFN as one expert
 // backward
 hipError_t launch_bwd_route(const Plan &p, hipStream_t s);      // idx -> counts, permutation
 hipError_t launch_bwd_gather(const Plan &p, hipStream_t s);     // x and gate*dout rows, permuted

@@ -298,6 +298,30 @@ hipError_t launch_permute(const Plan &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The dense FFN as one expert that every token uses: identity permutation,
+// one segment of T rows, ceil(T / chunk_rows) chunks.
+__global__ void dense_route_kernel(int64_t T, int chunk_rows, int32_t *__restrict__ tok,
+                                   int32_t *__restrict__ offs, int32_t *__restrict__ chunk_off,
+                                   int32_t *__restrict__ meta) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < T) tok[i] = static_cast<int32_t>(i);
+  if (i == 0) {
+    const int nch = static_cast<int>((T + chunk_rows - 1) / chunk_rows);
+    offs[0] = 0;
+    offs[1] = static_cast<int32_t>(T);
+    chunk_off[0] = 0;
+    chunk_off[1] = nch;
+    meta[0] = nch;
+    meta[1] = static_cast<int32_t>(T);
+  }
+}
+
+hipError_t launch_dense_route(const Plan &p, hipStream_t s) {
+  hipLaunchKernelGGL(dense_route_kernel, dim3(static_cast<unsigned>((p.T + 255) / 256)), dim3(256),
+                     0, s, p.T, p.nbmax * 32, p.tok, p.offs, p.chunk_off, p.meta);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero_counts(const Plan &p, hipStream_t s) {
   hipLaunchKernelGGL(zero_int_kernel, dim3((p.E + 255) / 256), dim3(256), 0, s, p.counts, p.E);
   return hipGetLastError();
