@@ -85,24 +85,30 @@ def cpu_model():
 # and WRITE_SIZE in their own runs and kept in a committed summary together
 # with the hash of the kernel source it was measured on; a summary taken on
 # another version of the kernel is not reported.
-def traffic_file(workload, fp8):
-    kind = "gemm8" if fp8 else "gemm"
-    return os.path.join(ROOT, "profiles", f"{kind}_gate_up_{workload}_hbm_traffic.txt")
+KERNEL_SOURCES = {"gemm": ("gemm.hip", "gemm_common.h"),
+                  "gemm8": ("gemm_fp8.hip", "gemm_common.h"),
+                  "wgrad": ("gemm_bwd.hip", "gemm_common.h")}
 
 
-def kernel_source_hash(fp8=False):
-    """sha256 over the gate/up GEMM kernel's sources (gemm.hip or gemm_fp8.hip,
-    and gemm_common.h)."""
+def traffic_file(workload, kind):
+    name = {"gemm": "gemm_gate_up", "gemm8": "gemm8_gate_up", "wgrad": "wgrad_gate_up"}[kind]
+    return os.path.join(ROOT, "profiles", f"{name}_{workload}_hbm_traffic.txt")
+
+
+def kernel_source_hash(kind="gemm"):
+    """sha256 over the sources of the kernel whose traffic is reported
+    (gate/up GEMM: gemm.hip or gemm_fp8.hip; weight-gradient GEMM:
+    gemm_bwd.hip; each with gemm_common.h)."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("gemm_fp8.hip" if fp8 else "gemm.hip", "gemm_common.h"):
+    for f in KERNEL_SOURCES[kind]:
         h.update(open(os.path.join(ROOT, "zero_computation_expert_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
 
-def measured_traffic(workload, fp8=False):
-    path = traffic_file(workload, fp8)
+def measured_traffic(workload, kind="gemm"):
+    path = traffic_file(workload, kind)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -110,7 +116,7 @@ def measured_traffic(workload, fp8=False):
         if ":" in line and not line.startswith(" "):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_hash(fp8):
+    if fields.get("kernel_source_sha256") != kernel_source_hash(kind):
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
@@ -289,7 +295,8 @@ def backward_bench(args, cfg, inp, dev):
         "roofline": {"bound": "hbm", "kernel": "wgrad_kernel (dW_gate += dG^T X, dW_up += dU^T X; "
                      "fp32 read-modify-write of the gradient)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(cfg.name, "wgrad"),
                      "algorithmic_bytes_per_launch": per_launch,
                      "avg_launch_ms": round(launch_ms, 4)},
         "step_hbm_frac": round(alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -472,7 +479,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(cfg.name, args.fp8),
+                "traffic": measured_traffic(cfg.name, "gemm8" if args.fp8 else "gemm"),
                 "algorithmic_bytes_per_launch": alg["gate_up"]["bytes"],
                 "avg_launch_ms": round(stage_avg["gate_up"], 4)}
     kernels = {}
