@@ -478,17 +478,11 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs &g, int e, int r0, in
     const int col = n0 + i * 32 + (lane & 3) * 8;
     b.off[i] = col < g.Ncols ? static_cast<uint32_t>(b.row) * g.ldq * 2 + col * 2 : kOOB;
   }
-  char *const w[3] = {s_w[0] + wave * kWaveRowBytes, s_w[1] + wave * kWaveRowBytes,
-                      s_w[2] + wave * kWaveRowBytes};
-  floatx16 acc[2][NBR];
-  k_loop<true, NBR>(acc, a.nks1, w, tl, lane, [&](int pos, int ks) {
-    n_load<NBR>(tl[pos], b, ks, wave);
-    mn_load(w[pos], a, ks);
-  });
-  // ---- epilogue: C[m, n] += acc (fp32 read-modify-write; every element of
-  // the output has one owner per launch).  All of the tile's old values are
-  // loaded before the first store, so their latencies overlap (stores and
-  // loads to one array would otherwise be kept in program order). ----
+  // The fp32 read-modify-write of C[m, n] += acc (every element has one
+  // owner per launch): the tile's old values are loaded before the K loop,
+  // so their HBM latency overlaps the operand stream (the loop's explicit
+  // waits count them: they complete in order before the first step's
+  // loads), and no branch splits the batch.
   // Buffer loads and stores with out-of-range offsets for the tile's edges:
   // no branches, so nothing splits the batch.
   const __amdgpu_buffer_rsrc_t rc =
@@ -498,15 +492,31 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs &g, int e, int r0, in
     const int m = m_base + a2 * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
     return (m < g.M && n < g.Ncols) ? static_cast<uint32_t>(m * g.Ncols + n) * 4u : kOOB;
   };
+  // the first kPre 32-column blocks' old values are loaded before the K
+  // loop (what the register file holds beside the loop), the rest after it
+  constexpr int kPre = NBR < 2 ? NBR : 2;
   float old[NBR][32];
-#pragma unroll
-  for (int nb = 0; nb < NBR; ++nb)
+  auto load_old = [&](int nb) {
 #pragma unroll
     for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         old[nb][a2 * 16 + i] = __uint_as_float(static_cast<uint32_t>(
             __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(coff(nb, a2, i)), 0, 0)));
+  };
+#pragma unroll
+  for (int nb = 0; nb < kPre; ++nb) load_old(nb);
+  asm volatile("" ::: "memory");
+  char *const w[3] = {s_w[0] + wave * kWaveRowBytes, s_w[1] + wave * kWaveRowBytes,
+                      s_w[2] + wave * kWaveRowBytes};
+  floatx16 acc[2][NBR];
+  k_loop<true, NBR>(acc, a.nks1, w, tl, lane, [&](int pos, int ks) {
+    n_load<NBR>(tl[pos], b, ks, wave);
+    mn_load(w[pos], a, ks);
+  });
+  // ---- epilogue: C[m, n] += acc ----
+#pragma unroll
+  for (int nb = kPre; nb < NBR; ++nb) load_old(nb);
 #pragma unroll
   for (int nb = 0; nb < NBR; ++nb)
 #pragma unroll
