@@ -29,7 +29,7 @@ def bf16_np(t):
     return synth.bf16_bits_to_f32(P.to_np(t))
 
 
-@pytest.mark.parametrize("T,d,Id", [(300, 256, 640), (37, 128, 96), (1, 64, 64)])
+@pytest.mark.parametrize("T,d,Id", [(300, 256, 640), (37, 128, 96), (1, 64, 64), (170, 200, 72)])
 def test_dense_ffn_parity(T, d, Id):
     cfg = synth.Config("dense", T=T, d=d, I=64, N=1, Z=1, k=1, dtype="bf16", seed=62)
     w = synth.host_dense(cfg, Id)
