@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(256) bwd_gather_kernel(const bf16_t *__restric
   for (int i = 0; i < 4; ++i) {
     const float lo = gt * __uint_as_float(w[i] << 16);
     const float hi = gt * __uint_as_float(w[i] & 0xFFFF0000u);
-    o[i] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    o[i] = pack_bf16x2(lo, hi);
   }
   *reinterpret_cast<uint4 *>(dyp + dst) = make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -208,8 +208,7 @@ __global__ void __launch_bounds__(256) dx_gather_kernel(
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    o[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i] + rr[2 * i])) |
-           (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1] + rr[2 * i + 1])) << 16);
+    o[i] = pack_bf16x2(acc[2 * i] + rr[2 * i], acc[2 * i + 1] + rr[2 * i + 1]);
   *reinterpret_cast<uint4 *>(dx + t * d + c) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 

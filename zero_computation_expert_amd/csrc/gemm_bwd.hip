@@ -338,7 +338,7 @@ __device__ __forceinline__ void dgrad_tile(const DgradArgs &g, const TileLoc &t,
           const uint32_t gb = (j & 1) ? (gw[j >> 1] & 0xFFFF0000u) : (gw[j >> 1] << 16);
           const uint32_t ub = (j & 1) ? (uw[j >> 1] & 0xFFFF0000u) : (uw[j >> 1] << 16);
           const float gg = __uint_as_float(gb), uu = __uint_as_float(ub);
-          const float sg = 1.0f / (1.0f + expf(-gg));
+          const float sg = sigmoid_hw(gg);
           const float v = acc[a2][nb][gi * 4 + j];
           hh[j] = gg * sg * uu;
           dsum += v * hh[j];  // zero for rows past the tile (G, U read as zeros)
@@ -347,9 +347,7 @@ __device__ __forceinline__ void dgrad_tile(const DgradArgs &g, const TileLoc &t,
           du[j] = dh * gg * sg;
         }
         auto pack = [](const float (&f)[4]) {
-          return make_uint2(
-              static_cast<uint32_t>(f32_to_bf16(f[0])) | (static_cast<uint32_t>(f32_to_bf16(f[1])) << 16),
-              static_cast<uint32_t>(f32_to_bf16(f[2])) | (static_cast<uint32_t>(f32_to_bf16(f[3])) << 16));
+          return make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
         };
         const int o = static_cast<int>(eoff(nb, a2, gi));
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));

@@ -56,13 +56,19 @@ __device__ __forceinline__ void store4<float>(float *dst, float a, float b, floa
 }
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t *dst, float a, float b, float c, float d) {
-  uint2 v;
-  v.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-  v.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
-  *reinterpret_cast<uint2 *>(dst) = v;
+  *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// Logistic sigmoid 1 / (1 + e^-x) from the hardware base-2 exponential and
+// reciprocal (about 1 ulp each; e^-x = 2^(-x log2 e)).  Large negative x
+// gives 2^(+big) = inf and a reciprocal of 0, large positive x gives 1.
+// Every caller rounds the result's products to bfloat16 or FP8.
+__device__ __forceinline__ float sigmoid_hw(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
+
+// SwiGLU of one gate/up pair: silu(g) * u = g * sigmoid(g) * u.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g * sigmoid_hw(g) * u; }
 
 constexpr int kThreads = 256;                  // 4 waves, each with two 32-row weight blocks
 constexpr int kWaveRowBytes = 64 * 128;        // one K-step of a wave's 64 weight rows

@@ -24,12 +24,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bfloat16 (NaN kept quiet).
+// fp32 -> bfloat16, rounded to nearest even by the gfx950 conversion
+// instruction (v_cvt_pk_bf16_f32; NaN stays NaN).  pack_bf16x2 converts two
+// values into one 32-bit word, lo in the low half.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_hw v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
+}
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return static_cast<bf16_t>(pack_bf16x2(f, 0.0f));
 }
 
 template <typename T>
