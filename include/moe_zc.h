@@ -61,8 +61,8 @@ typedef enum {
 
 /* Problem sizes.  Limits: T >= 0; d >= 8 and I >= 8, both multiples of 8;
  * N >= 0, Z >= 0, 1 <= N + Z <= 2048; 1 <= k <= min(64, N + Z);
- * T * k < 2^31; T * d and I * d (times the element size) below 2 GiB.
- * I is ignored when N == 0. */
+ * T * k < 2^31; T * d and I * d (times the element size) below 2 GiB;
+ * d and I at most 2^22.  I is ignored when N == 0. */
 typedef struct {
   int64_t T;     /* tokens                                   */
   int32_t d;     /* model width                               */
@@ -201,7 +201,7 @@ void moe_zc_timer_destroy(moe_zc_timer *timer);
  *
  * moe_zc_dense_ffn: out[t] = W2 (silu(W1 x[t]) * (W3 x[t])), bfloat16,
  *   x [T, d], W1 and W3 [I_dense, d], W2 [d, I_dense], out [T, d] (must not
- *   overlap x); d and I_dense multiples of 8; workspace of
+ *   overlap x); d and I_dense multiples of 8, at most 2^22; workspace of
  *   moe_zc_dense_workspace_bytes(T, d, I_dense) bytes, 256-byte aligned.
  *   It runs on the expert GEMM kernels as one expert that every token uses.
  *

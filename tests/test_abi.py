@@ -72,6 +72,8 @@ EINVAL, EDTYPE, EALIGN, ENOSPC = -1, -2, -3, -4
     (D(T=1 << 28, k=8), EINVAL),             # T * k >= 2^31
     (D(T=1 << 20, d=1024, k=2), EINVAL),     # x is 2 GiB of bf16
     (D(I=1 << 17, d=8192), EINVAL),          # one expert matrix is 2 GiB
+    (D(T=8, d=(1 << 22) + 8, I=8), EINVAL),  # d above 2^22
+    (D(T=8, d=8, I=(1 << 22) + 8), EINVAL),  # I above 2^22
 ])
 def test_invalid_dims(dims, expect):
     assert moe.lib().moe_zc_workspace_bytes(ctypes.byref(dims)) == 0
@@ -261,6 +263,7 @@ def test_dense_ffn_rejects():
 
     assert dense(d=100) == EALIGN
     assert dense(Id=60) == EALIGN
+    assert dense(T=8, d=8, Id=(1 << 22) + 8) == EINVAL   # width above 2^22
     assert dense(x=None) == EINVAL
     assert dense(out=A + 32) == EINVAL   # out overlaps x
     assert dense(w2=4 * A + 4) == EALIGN

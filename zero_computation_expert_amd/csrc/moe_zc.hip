@@ -36,6 +36,12 @@ static bool dims_ok(const moe_zc_dims *dm, int *status) {
     *status = MOE_ZC_EINVAL;
     return false;
   }
+  // The expert GEMM epilogues store through tile-relative 32-bit offsets
+  // (up to 160 rows of d or I elements).
+  if (dm->d > kMaxWidth || (dm->N > 0 && dm->I > kMaxWidth)) {
+    *status = MOE_ZC_EINVAL;
+    return false;
+  }
   if (dm->d % 8 != 0 || (dm->N > 0 && dm->I % 8 != 0)) {
     *status = MOE_ZC_EALIGN;
     return false;
@@ -439,7 +445,7 @@ static int backward_impl(const moe_zc_dims *dm, const void *x, const void *w_rou
 static bool dense_dims_ok(int64_t T, int d, int Id) {
   const int64_t lim = int64_t(1) << 31;
   return T >= 0 && d >= 8 && Id >= 8 && d % 8 == 0 && Id % 8 == 0 && T * d * 2 < lim &&
-         static_cast<int64_t>(Id) * d * 2 < lim && T < lim;
+         static_cast<int64_t>(Id) * d * 2 < lim && T < lim && d <= kMaxWidth && Id <= kMaxWidth;
 }
 
 static size_t layout_dense(int64_t T, int Id, char *base, Plan *p) {

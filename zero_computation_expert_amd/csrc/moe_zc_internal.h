@@ -16,6 +16,7 @@ constexpr int kTokPerBlk = 16;  // tokens per top-k / permutation block (one wav
 constexpr int kMaxE = 2048;     // experts the top-k kernel holds in registers
 constexpr int kMaxK = 64;       // slots per token (one lane per slot)
 constexpr int kMaxKb8 = 96;    // FP8 path: 128-wide K blocks per row (d, I <= 12288)
+constexpr int kMaxWidth = 1 << 22;  // d and I (expert GEMM epilogues use tile-relative 32-bit offsets)
 
 // bfloat16 is carried as its 16-bit pattern.
 typedef uint16_t bf16_t;
