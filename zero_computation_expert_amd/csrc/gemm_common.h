@@ -219,4 +219,94 @@ __device__ __forceinline__ int xcd_tile(int ntiles) {
   return v < ntiles ? v : -1;
 }
 
+// bf16 epilogue of the expert modes, staged through LDS.  Written straight
+// from the MFMA layout, every store instruction would put 16-byte pieces into
+// 32 different token rows; instead each wave writes its 64 (DOWN) or 32
+// (GATE_UP; G and U for GATE_UP_RAW) output features of every token row of
+// the tile into its own 128-byte LDS rows (16-byte chunks XOR-swizzled by
+// row), then stores whole row segments, 8 (or 4) lanes x 16 bytes per row.
+// Rows past the chunk and features past nrows fall outside the buffer range
+// and are dropped.  Offsets are tile-relative 32-bit values (the validator
+// caps d and I so that 160 rows of either fit).
+template <int MODE, int NBR>
+__device__ __forceinline__ void stage_epilogue(const GemmArgs &g, const TileLoc &t,
+                                               const floatx16 (&acc)[2][NBR], char *st,
+                                               int featbase, int r, int h, int lane) {
+  // ---- registers -> LDS
+#pragma unroll
+  for (int nb = 0; nb < NBR; ++nb) {
+    const int col = nb * 32 + r;
+    char *row = st + col * 128;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      if (MODE == MODE_DOWN) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int c = a * 4 + gi;
+          const floatx16 &v = acc[a][nb];
+          *reinterpret_cast<uint2 *>(row + ((c ^ (col & 7)) << 4) + h * 8) =
+              make_uint2(pack_bf16x2(v[gi * 4 + 0], v[gi * 4 + 1]),
+                         pack_bf16x2(v[gi * 4 + 2], v[gi * 4 + 3]));
+        }
+      } else if (MODE == MODE_GATE_UP) {
+        const floatx16 &ga = acc[0][nb];
+        const floatx16 &ua = acc[1][nb];
+        *reinterpret_cast<uint2 *>(row + ((gi ^ (col & 7)) << 4) + h * 8) =
+            make_uint2(pack_bf16x2(silu_mul(ga[gi * 4 + 0], ua[gi * 4 + 0]),
+                                   silu_mul(ga[gi * 4 + 1], ua[gi * 4 + 1])),
+                       pack_bf16x2(silu_mul(ga[gi * 4 + 2], ua[gi * 4 + 2]),
+                                   silu_mul(ga[gi * 4 + 3], ua[gi * 4 + 3])));
+      } else {  // GATE_UP_RAW: G in chunks 0..3, U in chunks 4..7
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int c = a * 4 + gi;
+          const floatx16 &v = acc[a][nb];
+          *reinterpret_cast<uint2 *>(row + ((c ^ (col & 7)) << 4) + h * 8) =
+              make_uint2(pack_bf16x2(v[gi * 4 + 0], v[gi * 4 + 1]),
+                         pack_bf16x2(v[gi * 4 + 2], v[gi * 4 + 3]));
+        }
+      }
+    }
+  }
+  // ---- LDS -> HBM, whole row segments
+  const uint32_t rowb = static_cast<uint32_t>(g.out_ld) * 2;
+  const uint32_t tbytes = static_cast<uint32_t>(t.mcount) * rowb;
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(static_cast<bf16_t *>(g.out) + static_cast<int64_t>(t.m0) * g.out_ld, tbytes);
+  if (MODE == MODE_GATE_UP) {
+    // 64 bytes per row: 4 lanes per row, 16 rows per instruction
+    const int c = lane & 3;
+    const int f0 = featbase + c * 8;
+    const uint32_t fo = f0 < g.nrows ? static_cast<uint32_t>(f0) * 2 : kOOB;
+#pragma unroll
+    for (int i = 0; i < 2 * NBR; ++i) {
+      const int row = i * 16 + (lane >> 2);
+      const uint4 v = *reinterpret_cast<const uint4 *>(st + row * 128 + ((c ^ (row & 7)) << 4));
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, ro,
+                                             static_cast<int>(row * rowb + fo), 0, 0);
+    }
+  } else {
+    // 128 bytes per row: 8 lanes per row, 8 rows per instruction
+    const int c = lane & 7;
+    const int f0 = featbase + (MODE == MODE_DOWN ? c : (c & 3)) * 8;
+    const uint32_t fo = f0 < g.nrows ? static_cast<uint32_t>(f0) * 2 : kOOB;
+    __amdgpu_buffer_rsrc_t ru = ro;
+    if (MODE == MODE_GATE_UP_RAW)
+      ru = make_rsrc(static_cast<bf16_t *>(g.out2) + static_cast<int64_t>(t.m0) * g.out_ld, tbytes);
+#pragma unroll
+    for (int i = 0; i < 4 * NBR; ++i) {
+      const int row = i * 8 + (lane >> 3);
+      const uint4 v = *reinterpret_cast<const uint4 *>(st + row * 128 + ((c ^ (row & 7)) << 4));
+      const u32x4 d = u32x4{v.x, v.y, v.z, v.w};
+      const uint32_t o = row * rowb + fo;
+      if (MODE == MODE_DOWN) {
+        __builtin_amdgcn_raw_buffer_store_b128(d, ro, static_cast<int>(o), 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(d, ro, static_cast<int>(c < 4 ? o : kOOB), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d, ru, static_cast<int>(c < 4 ? kOOB : o), 0, 0);
+      }
+    }
+  }
+}
+
 }  // namespace moezc

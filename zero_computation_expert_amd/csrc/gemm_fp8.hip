@@ -296,21 +296,11 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
   // Lane (r, h) holds, for column r of each 32x32 tile, rows
   // gi*8 + h*4 + [0, 4) in acc elements gi*4 .. gi*4+3.
   if (MODE == MODE8_DOWN) {
-#pragma unroll
-    for (int nb = 0; nb < NBR; ++nb) {
-      const int col = nb * 32 + r;
-      if (col >= mcount) continue;
-      bf16_t *orow = static_cast<bf16_t *>(g.out) + (static_cast<int64_t>(m0) + col) * g.out_ld;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const int row = rowbase[a] + gi * 8 + h * 4;
-          if (row < g.nrows)
-            store4<bf16_t>(orow + row, acc[a][nb][gi * 4 + 0], acc[a][nb][gi * 4 + 1],
-                           acc[a][nb][gi * 4 + 2], acc[a][nb][gi * 4 + 3]);
-        }
-    }
+    // bf16 Y staged through wave-private LDS rows, as in the bf16 kernel; the
+    // barrier covers every wave's last loads and token-tile writes
+    tile_barrier();
+    char *const stg = wave == 0 ? s_tile[0] : (wave == 1 ? s_tile[1] : (wave == 2 ? s_w0 : s_w1));
+    stage_epilogue<MODE_DOWN, NBR>(g, t, acc, stg, rowbase[0], r, h, lane);
     return;
   }
 
@@ -331,7 +321,10 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
   }
   tile_barrier();
   const int nkb_i = g.nrows / 128;  // H exponent row length (I / 128)
-  fp8_t *hq = static_cast<fp8_t *>(g.out);
+  // The workgroup's 128 quantized features of a token row are one 128-byte
+  // line: the four waves write their 32 bytes of every row into one shared
+  // LDS tile (16-byte chunks XOR-swizzled by row), then store whole lines.
+  char *const hs = s_tile[0];
 #pragma unroll
   for (int nb = 0; nb < NBR; ++nb) {
     const int col = nb * 32 + r;
@@ -341,21 +334,37 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
       amax = fmaxf(amax, reinterpret_cast<const float *>(s_w0 + w * kWaveRowBytes)[nb * 32 + r]);
     const int ex = block_exponent(amax);
     const float inv = pow2_neg(ex);
-    if (col >= mcount) continue;
-    fp8_t *orow = hq + (static_cast<int64_t>(m0) + col) * g.out_ld;
+    char *hrow = hs + col * 128;
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-      const int row = rowbase[0] + gi * 8 + h * 4;
       const floatx16 &ga = acc[0][nb];
       const floatx16 &ua = acc[1][nb];
-      *reinterpret_cast<uint32_t *>(orow + row) =
+      const int q = wave * 2 + (gi >> 1);  // 16-byte chunk of features wave*32 + gi*8 + h*4
+      *reinterpret_cast<uint32_t *>(hrow + ((q ^ (col & 7)) << 4) + (gi & 1) * 8 + h * 4) =
           pack4_e4m3(silu_mul(ga[gi * 4 + 0], ua[gi * 4 + 0]) * inv,
                      silu_mul(ga[gi * 4 + 1], ua[gi * 4 + 1]) * inv,
                      silu_mul(ga[gi * 4 + 2], ua[gi * 4 + 2]) * inv,
                      silu_mul(ga[gi * 4 + 3], ua[gi * 4 + 3]) * inv);
     }
-    if (wave == 0 && h == 0)
+    if (wave == 0 && h == 0 && col < mcount)
       g.out_s[(static_cast<int64_t>(m0) + col) * nkb_i + rb] = static_cast<uint8_t>(ex + 127);
+  }
+  tile_barrier();
+  // rows (4i + wave)*8 + lane/8, 16-byte chunk lane%8; rows past the chunk
+  // fall outside the tile's buffer range and are dropped
+  const uint32_t tbytes = static_cast<uint32_t>(mcount) * static_cast<uint32_t>(g.out_ld);
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(static_cast<fp8_t *>(g.out) + static_cast<int64_t>(m0) * g.out_ld, tbytes);
+  const int c = lane & 7;
+#pragma unroll
+  for (int i = 0; i < NBR; ++i) {
+    const int row = (i * 4 + wave) * 8 + (lane >> 3);
+    const uint4 v = *reinterpret_cast<const uint4 *>(hs + row * 128 + ((c ^ (row & 7)) << 4));
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{v.x, v.y, v.z, v.w}, ro,
+        static_cast<int>(static_cast<uint32_t>(row) * static_cast<uint32_t>(g.out_ld) +
+                         static_cast<uint32_t>(rb) * 128 + c * 16),
+        0, 0);
   }
 }
 
