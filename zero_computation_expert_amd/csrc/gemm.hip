@@ -270,7 +270,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     char *const st = wave == 0 ? tl[0] : (wave == 1 ? tl[1] : (wave == 2 ? tl[2] : s_w[0]));
-    stage_epilogue<MODE, NBR>(g, t, acc, st, rowbase[0], r, h, lane);
+    stage_epilogue<MODE, NBR>(g.out, g.out2, g.out_ld, g.nrows, t, acc, st, rowbase[0], r, h, lane);
     return;
   }
   // fp32 storage and the router's partial logits: straight from registers.

@@ -369,6 +369,14 @@ __device__ __forceinline__ void dgrad_tile(const DgradArgs &g, const TileLoc &t,
         sum += reinterpret_cast<const float *>(s_w[0] + wv * kWaveRowBytes)[c];
       g.dpart[static_cast<int64_t>(t.rb) * g.dpart_stride + t.m0 + c] = sum;
     }
+  } else if (MODE == BW_DX) {
+    // bf16 dx rows of the tile (the wave's 64 contiguous columns from
+    // m_base) staged through wave-private LDS rows in the idle ring, as in
+    // the forward expert GEMMs
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    char *const st = wave == 0 ? tl[0] : (wave == 1 ? tl[1] : (wave == 2 ? tl[2] : s_w[0]));
+    stage_epilogue<MODE_DOWN, NBR>(g.out, nullptr, g.ldo, g.M, t, acc, st, m_base, r, h, lane);
   } else {
 #pragma unroll
     for (int nb = 0; nb < NBR; ++nb) {
@@ -382,12 +390,8 @@ __device__ __forceinline__ void dgrad_tile(const DgradArgs &g, const TileLoc &t,
           const int m = m_base + a2 * 32 + gi * 8 + h * 4;
           if (m >= g.M) continue;
           const floatx16 &v = acc[a2][nb];
-          if (MODE == BW_DX)
-            store4<bf16_t>(static_cast<bf16_t *>(g.out) + orow + m, v[gi * 4], v[gi * 4 + 1],
-                           v[gi * 4 + 2], v[gi * 4 + 3]);
-          else
-            store4<float>(static_cast<float *>(g.out) + orow + m, v[gi * 4], v[gi * 4 + 1],
-                          v[gi * 4 + 2], v[gi * 4 + 3]);
+          store4<float>(static_cast<float *>(g.out) + orow + m, v[gi * 4], v[gi * 4 + 1],
+                        v[gi * 4 + 2], v[gi * 4 + 3]);
         }
     }
   }

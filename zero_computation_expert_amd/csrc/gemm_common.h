@@ -228,10 +228,12 @@ __device__ __forceinline__ int xcd_tile(int ntiles) {
 // Rows past the chunk and features past nrows fall outside the buffer range
 // and are dropped.  Offsets are tile-relative 32-bit values (the validator
 // caps d and I so that 160 rows of either fit).
+// out (and out2 for GATE_UP_RAW): bf16 [rows, out_ld], the tile's rows
+// starting at t.m0; features at or past nrows are not stored.
 template <int MODE, int NBR>
-__device__ __forceinline__ void stage_epilogue(const GemmArgs &g, const TileLoc &t,
-                                               const floatx16 (&acc)[2][NBR], char *st,
-                                               int featbase, int r, int h, int lane) {
+__device__ __forceinline__ void stage_epilogue(void *out, void *out2, int out_ld, int nrows,
+                                               const TileLoc &t, const floatx16 (&acc)[2][NBR],
+                                               char *st, int featbase, int r, int h, int lane) {
   // ---- registers -> LDS
 #pragma unroll
   for (int nb = 0; nb < NBR; ++nb) {
@@ -269,15 +271,15 @@ __device__ __forceinline__ void stage_epilogue(const GemmArgs &g, const TileLoc 
     }
   }
   // ---- LDS -> HBM, whole row segments
-  const uint32_t rowb = static_cast<uint32_t>(g.out_ld) * 2;
+  const uint32_t rowb = static_cast<uint32_t>(out_ld) * 2;
   const uint32_t tbytes = static_cast<uint32_t>(t.mcount) * rowb;
   const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(static_cast<bf16_t *>(g.out) + static_cast<int64_t>(t.m0) * g.out_ld, tbytes);
+      make_rsrc(static_cast<bf16_t *>(out) + static_cast<int64_t>(t.m0) * out_ld, tbytes);
   if (MODE == MODE_GATE_UP) {
     // 64 bytes per row: 4 lanes per row, 16 rows per instruction
     const int c = lane & 3;
     const int f0 = featbase + c * 8;
-    const uint32_t fo = f0 < g.nrows ? static_cast<uint32_t>(f0) * 2 : kOOB;
+    const uint32_t fo = f0 < nrows ? static_cast<uint32_t>(f0) * 2 : kOOB;
 #pragma unroll
     for (int i = 0; i < 2 * NBR; ++i) {
       const int row = i * 16 + (lane >> 2);
@@ -289,10 +291,10 @@ __device__ __forceinline__ void stage_epilogue(const GemmArgs &g, const TileLoc 
     // 128 bytes per row: 8 lanes per row, 8 rows per instruction
     const int c = lane & 7;
     const int f0 = featbase + (MODE == MODE_DOWN ? c : (c & 3)) * 8;
-    const uint32_t fo = f0 < g.nrows ? static_cast<uint32_t>(f0) * 2 : kOOB;
+    const uint32_t fo = f0 < nrows ? static_cast<uint32_t>(f0) * 2 : kOOB;
     __amdgpu_buffer_rsrc_t ru = ro;
     if (MODE == MODE_GATE_UP_RAW)
-      ru = make_rsrc(static_cast<bf16_t *>(g.out2) + static_cast<int64_t>(t.m0) * g.out_ld, tbytes);
+      ru = make_rsrc(static_cast<bf16_t *>(out2) + static_cast<int64_t>(t.m0) * out_ld, tbytes);
 #pragma unroll
     for (int i = 0; i < 4 * NBR; ++i) {
       const int row = i * 8 + (lane >> 3);

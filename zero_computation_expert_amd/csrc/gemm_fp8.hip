@@ -300,7 +300,8 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
     // barrier covers every wave's last loads and token-tile writes
     tile_barrier();
     char *const stg = wave == 0 ? s_tile[0] : (wave == 1 ? s_tile[1] : (wave == 2 ? s_w0 : s_w1));
-    stage_epilogue<MODE_DOWN, NBR>(g, t, acc, stg, rowbase[0], r, h, lane);
+    stage_epilogue<MODE_DOWN, NBR>(g.out, nullptr, g.out_ld, g.nrows, t, acc, stg, rowbase[0], r,
+                                   h, lane);
     return;
   }
 
