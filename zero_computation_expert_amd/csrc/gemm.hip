@@ -144,12 +144,12 @@ __device__ __forceinline__ void compute(floatx16 (&acc)[2][NBR], const char *slo
 // barriers keep the groups apart), so once only the NBR + 8 loads of step
 // ks + 2 remain outstanding, this wave's loads of step ks + 1 have landed;
 // the barrier then covers every wave's.
-template <typename T, int NBR, int S>
+template <typename T, int NBR, int S, int WAUX>
 __device__ __forceinline__ void kstep(int ks, floatx16 (&acc)[2][NBR], char *const (&w)[3],
                                       char *const (&tl)[3], const TileState<NBR> &st,
                                       const uint32_t (&tvo)[NBR], int r, int h, int wave) {
   load_t<T, NBR>(tl[(S + 2) % 3], tvo, st, ks + 2, wave);
-  load_w<T, NBR>(w[(S + 2) % 3], st, ks + 2);
+  load_w<T, NBR, WAUX>(w[(S + 2) % 3], st, ks + 2);
   asm volatile("" ::: "memory");
   compute<T, NBR>(acc, w[S], tl[S], r, h);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBR + 8));
@@ -165,6 +165,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
                                           char *const (&s_w)[3], char *const (&tl)[3]) {
   constexpr int KC = 128 / sizeof(T);  // K elements per step (128 bytes per row)
   constexpr uint32_t ES = sizeof(T);
+  // the router's weights are read by every token tile; expert weights once
+  constexpr int kWAux = MODE == MODE_ROUTER ? kReuse : kStreamOnce;
   const int e = t.e, rb = t.rb, m0 = t.m0, mcount = t.mcount;
   const uint32_t kbyte0 = static_cast<uint32_t>(t.k0) * ES;  // first byte of the K range in a row
 
@@ -236,10 +238,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
 
   // ---- prologue: steps 0 and 1 in the same per-step groups as the loop ----
   load_t<T, NBR>(tl[0], tvo, st, 0, wave);
-  load_w<T, NBR>(w[0], st, 0);
+  load_w<T, NBR, kWAux>(w[0], st, 0);
   asm volatile("" ::: "memory");
   load_t<T, NBR>(tl[1], tvo, st, 1, wave);
-  load_w<T, NBR>(w[1], st, 1);
+  load_w<T, NBR, kWAux>(w[1], st, 1);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBR + 8));
   asm volatile("" ::: "memory");
@@ -249,12 +251,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
   // ---- main loop, unrolled by the 3 buffers -----------------------------
   int ks = 0;
   for (; ks + 3 <= nks; ks += 3) {
-    kstep<T, NBR, 0>(ks, acc, w, tl, st, tvo, r, h, wave);
-    kstep<T, NBR, 1>(ks + 1, acc, w, tl, st, tvo, r, h, wave);
-    kstep<T, NBR, 2>(ks + 2, acc, w, tl, st, tvo, r, h, wave);
+    kstep<T, NBR, 0, kWAux>(ks, acc, w, tl, st, tvo, r, h, wave);
+    kstep<T, NBR, 1, kWAux>(ks + 1, acc, w, tl, st, tvo, r, h, wave);
+    kstep<T, NBR, 2, kWAux>(ks + 2, acc, w, tl, st, tvo, r, h, wave);
   }
-  if (ks < nks) kstep<T, NBR, 0>(ks, acc, w, tl, st, tvo, r, h, wave);
-  if (ks + 1 < nks) kstep<T, NBR, 1>(ks + 1, acc, w, tl, st, tvo, r, h, wave);
+  if (ks < nks) kstep<T, NBR, 0, kWAux>(ks, acc, w, tl, st, tvo, r, h, wave);
+  if (ks + 1 < nks) kstep<T, NBR, 1, kWAux>(ks + 1, acc, w, tl, st, tvo, r, h, wave);
 
   // Drain the prefetches past the end of K (they read zeros into buffers
   // that are never read) so that no direct-to-LDS write is still in flight

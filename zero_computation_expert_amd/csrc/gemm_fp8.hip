@@ -108,7 +108,7 @@ __device__ __forceinline__ void kstep8(int ks, floatx16 (&acc)[2][NBR], char *w0
   char *const slot_now = S % 3 == 0 ? w0 : (S % 3 == 1 ? w1 : w2);
   char *const slot_next = (S + 2) % 3 == 0 ? w0 : ((S + 2) % 3 == 1 ? w1 : w2);
   load_b<fp8_t, NBR>(xr[S & 1], st, ks + 2);
-  load_w<fp8_t, NBR>(slot_next, st, ks + 2);
+  load_w<fp8_t, NBR, kStreamOnce>(slot_next, st, ks + 2);
   compute8<NBR>(acc, slot_now, tile[ks & 1], sa0, sa1, sbc, nkb, ks, r, h);
   store_b<NBR>(tile[(ks + 1) & 1], xr[(S + 1) & 1], brow, bp);
   tile_barrier();
@@ -267,11 +267,11 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
 
   // prologue: the loads of steps 0 and 1 in the main loop's group order
   load_b<fp8_t, NBR>(xr[0], st, 0);
-  load_w<fp8_t, NBR>(w0, st, 0);
+  load_w<fp8_t, NBR, kStreamOnce>(w0, st, 0);
   asm volatile("" ::: "memory");
   store_b<NBR>(s_tile[0], xr[0], brow, bp);
   load_b<fp8_t, NBR>(xr[1], st, 1);
-  load_w<fp8_t, NBR>(w1, st, 1);
+  load_w<fp8_t, NBR, kStreamOnce>(w1, st, 1);
   tile_barrier();  // also publishes the exponent copies
 
   int ks = 0;
