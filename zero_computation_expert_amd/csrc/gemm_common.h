@@ -76,9 +76,10 @@ constexpr int kWSlotBytes = 4 * kWaveRowBytes; // one K-step of the workgroup's 
 constexpr int kPitch = 128;  // LDS bytes per token row (16-byte chunks XOR-swizzled by row)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: the load reads zeros
 // Cache policy of buffer accesses to data a launch touches once (the expert
-// weight streams, the weight gradients' read-modify-write): non-temporal, so
-// it does not evict the rows that are reused (token tiles, operands shared by
-// several tiles).  Measured: prod GATE_UP -3%, decode -11%.
+// weight streams, the GEMM outputs, the weight gradients' read-modify-write):
+// non-temporal, so it does not evict the rows that are reused (token tiles,
+// operands shared by several tiles).  Measured: prod GATE_UP -3 to -10%,
+// decode -11%; the outputs' stores another -1% (GATE_UP) and -5% (DOWN).
 constexpr int kStreamOnce = 2;  // NT
 constexpr int kReuse = 0;
 
@@ -291,7 +292,7 @@ __device__ __forceinline__ void stage_epilogue(void *out, void *out2, int out_ld
       const int row = i * 16 + (lane >> 2);
       const uint4 v = *reinterpret_cast<const uint4 *>(st + row * 128 + ((c ^ (row & 7)) << 4));
       __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, ro,
-                                             static_cast<int>(row * rowb + fo), 0, 0);
+                                             static_cast<int>(row * rowb + fo), 0, kStreamOnce);
     }
   } else {
     // 128 bytes per row: 8 lanes per row, 8 rows per instruction
@@ -308,10 +309,12 @@ __device__ __forceinline__ void stage_epilogue(void *out, void *out2, int out_ld
       const u32x4 d = u32x4{v.x, v.y, v.z, v.w};
       const uint32_t o = row * rowb + fo;
       if (MODE == MODE_DOWN) {
-        __builtin_amdgcn_raw_buffer_store_b128(d, ro, static_cast<int>(o), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d, ro, static_cast<int>(o), 0, kStreamOnce);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b128(d, ro, static_cast<int>(c < 4 ? o : kOOB), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(d, ru, static_cast<int>(c < 4 ? kOOB : o), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d, ro, static_cast<int>(c < 4 ? o : kOOB), 0,
+                                               kStreamOnce);
+        __builtin_amdgcn_raw_buffer_store_b128(d, ru, static_cast<int>(c < 4 ? kOOB : o), 0,
+                                               kStreamOnce);
       }
     }
   }

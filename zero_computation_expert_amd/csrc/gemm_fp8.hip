@@ -365,7 +365,7 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
         u32x4{v.x, v.y, v.z, v.w}, ro,
         static_cast<int>(static_cast<uint32_t>(row) * static_cast<uint32_t>(g.out_ld) +
                          static_cast<uint32_t>(rb) * 128 + c * 16),
-        0, 0);
+        0, kStreamOnce);
   }
 }
 
