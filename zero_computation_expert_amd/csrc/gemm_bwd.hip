@@ -57,6 +57,29 @@ __device__ __forceinline__ bf16x8_t tr_frag(const char *sub, int s, int lane) {
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// The MN operand's K-step in LDS: 64 K-rows of the wave's 64 columns, 128
+// bytes per row, 16-byte chunk c of row r stored at position c ^ mn_swz(r).
+// Besides the usual row & 7, rows with bit 1 set also flip chunk bit 2: the
+// 32 lanes of one pass of a transposing read cover rows r0 + [0, 4) of two
+// 4-chunk groups, and rows r0 and r0 + 2 share a bank half, so they must sit
+// in different chunk groups to keep the read free of bank conflicts.
+__device__ __forceinline__ int mn_swz(int row) { return (row & 7) ^ (((row >> 1) & 1) << 2); }
+
+// tr_frag for that layout: the same operand as tr_frag on a 32-column
+// sub-tile (columns a*32 ..), each lane's 4 columns located in the swizzled
+// 128-byte row (the second read is 4 rows further, with its own swizzle).
+__device__ __forceinline__ bf16x8_t tr_frag_mn(const char *region, int a, int s, int lane) {
+  const int grp = lane >> 4, l = lane & 15;
+  const int row = s * 16 + (grp >> 1) * 8 + (l >> 2);
+  const int col = a * 32 + (grp & 1) * 16 + (l & 3) * 4;
+  const int chunk = col >> 3, within = (col & 7) * 2;
+  const int o0 = row * 128 + ((chunk ^ mn_swz(row)) << 4) + within;
+  const int o1 = (row + 4) * 128 + ((chunk ^ mn_swz(row + 4)) << 4) + within;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(region + o0));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(region + o1));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // MFMA operand from the swizzled 128-byte-per-row token tile: row r, K
 // elements s*16 + h*8 + [0, 8) (chunk 2s + h, XOR-swizzled by r & 7).
 __device__ __forceinline__ bf16x8_t k_frag(const char *tb, int s, int r, int h) {
@@ -68,19 +91,20 @@ __device__ __forceinline__ void mfma(floatx16 &acc, const bf16x8_t &a, const bf1
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
 }
 
+template <int AUX = kReuse>
 __device__ __forceinline__ void dma16(const __amdgpu_buffer_rsrc_t &rs, char *lds_base,
                                       uint32_t off) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)lds_base, 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)lds_base, 16, off, 0, 0, AUX);
 #else
   (void)rs; (void)lds_base; (void)off;
 #endif
 }
 
 // ---- operand streams ------------------------------------------------------
-// An MN-contiguous operand, one wave's 64 columns (two sub-tiles) per K-step:
-// instruction i moves K-rows (i & 3)*16 + lane/4 of sub-tile i >> 2, 16
-// bytes (8 columns) per lane.  Up to two K halves (dx: W_gate then W_up),
+// An MN-contiguous operand, one wave's 64 columns per K-step: instruction i
+// moves K-rows i*8 + lane/8 whole (128 bytes: 8 lanes of 16 bytes, lane
+// position p loading chunk p ^ mn_swz(row)), so every read is full lines.  Up to two K halves (dx: W_gate then W_up),
 // each of `K` rows and its own buffer; a step past the half's rows, or
 // columns past the matrix, read zeros.
 struct MnStream {
@@ -91,17 +115,15 @@ struct MnStream {
   int K, nks1;       // rows per half, K-steps of the first half
 };
 
-// Default cache policy even for the expert weights of dgrad, which are read
-// once: each 128-byte line is read as two 64-byte halves by two instructions,
-// and with the non-temporal hint the second half missed again (prod dgrad
-// 5.4 -> 7.4 ms when tried).
+// AUX: the cache policy (the expert weights of dgrad are read once).
+template <int AUX>
 __device__ __forceinline__ void mn_load(char *region, const MnStream &a, int ks) {
   const int half = ks >= a.nks1 ? 1 : 0;
   const int kk = ks - half * a.nks1;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const bool ok = a.off[i] != kOOB && kk * 64 + a.row[i] < a.K;
-    dma16(a.rs[half], region + (i >> 2) * kSub + (i & 3) * 1024,
+    dma16<AUX>(a.rs[half], region + i * 1024,
           ok ? a.off[i] + static_cast<uint32_t>(kk) * a.step : kOOB);
   }
 }
@@ -158,7 +180,7 @@ __device__ __forceinline__ void compute(floatx16 (&acc)[2][NBR], const char *wa,
   bf16x8_t A[2][2], B[2][NBR];
   auto frags = [&](int s, int buf) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) A[buf][a] = tr_frag(wa + a * kSub, s, lane);
+    for (int a = 0; a < 2; ++a) A[buf][a] = tr_frag_mn(wa, a, s, lane);
 #pragma unroll
     for (int nb = 0; nb < NBR; ++nb)
       B[buf][nb] = B_TR ? tr_frag(tile + nb * kSub, s, lane) : k_frag(tb + nb * 32 * kPitch, s, r, h);
@@ -259,8 +281,8 @@ __device__ __forceinline__ void dgrad_tile(const DgradArgs &g, const TileLoc &t,
   a.nks1 = (g.K + 63) / 64;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    a.row[i] = (i & 3) * 16 + (lane >> 2);
-    const int col = m_base + (i >> 2) * 32 + (lane & 3) * 8;
+    a.row[i] = i * 8 + (lane >> 3);
+    const int col = m_base + ((lane & 7) ^ mn_swz(lane >> 3)) * 8;
     a.off[i] = col < g.M ? static_cast<uint32_t>(a.row[i]) * g.lda * 2 + col * 2 : kOOB;
   }
   // B: the tile's rows, K-contiguous
@@ -292,7 +314,7 @@ __device__ __forceinline__ void dgrad_tile(const DgradArgs &g, const TileLoc &t,
   floatx16 acc[2][NBR];
   k_loop<false, NBR>(acc, nks, w, tl, lane, [&](int pos, int ks) {
     k_load<NBR>(tl[pos], b, ks, wave);
-    mn_load(w[pos], a, ks);
+    mn_load<MODE == BW_DXR ? kReuse : kStreamOnce>(w[pos], a, ks);
   });
 
   // ---- epilogue: lane (r, h) holds column r, rows gi*8 + h*4 + [0, 4) ----
@@ -469,8 +491,8 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs &g, int e, int r0, in
   a.nks1 = (nrows + 63) / 64;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    a.row[i] = (i & 3) * 16 + (lane >> 2);
-    const int col = m_base + (i >> 2) * 32 + (lane & 3) * 8;
+    a.row[i] = i * 8 + (lane >> 3);
+    const int col = m_base + ((lane & 7) ^ mn_swz(lane >> 3)) * 8;
     a.off[i] = col < g.M ? static_cast<uint32_t>(a.row[i]) * g.ldp * 2 + col * 2 : kOOB;
   }
   NStream<NBR> b;
@@ -519,7 +541,7 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs &g, int e, int r0, in
   floatx16 acc[2][NBR];
   k_loop<true, NBR>(acc, a.nks1, w, tl, lane, [&](int pos, int ks) {
     n_load<NBR>(tl[pos], b, ks, wave);
-    mn_load(w[pos], a, ks);
+    mn_load<kReuse>(w[pos], a, ks);
   });
   // ---- epilogue: C[m, n] += acc ----
 #pragma unroll
