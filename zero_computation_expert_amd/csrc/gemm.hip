@@ -38,6 +38,12 @@
 //     (workgroups are dealt round-robin over the 8 XCDs): the row blocks of
 //     one expert share that expert's token rows in one L2, and the chunks of
 //     one row block share its weight rows.
+//   * Expert weights and the outputs are touched once per launch and carry
+//     the non-temporal cache hint, so they do not evict those token rows;
+//     the router's weights, read by every token tile, do not.
+//   * bf16 outputs leave through the idle ring: each wave stages its output
+//     features of every token row in LDS and stores whole row segments
+//     (stage_epilogue), instead of 16-byte pieces scattered over 32 rows.
 #include "gemm_common.h"
 
 namespace moezc {
@@ -275,7 +281,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
     stage_epilogue<MODE, NBR>(g.out, g.out2, g.out_ld, g.nrows, t, acc, st, rowbase[0], r, h, lane);
     return;
   }
-  // fp32 storage and the router's partial logits: straight from registers.
+  // fp32 storage and the router's partial logits: straight from registers
+  // (GATE_UP_RAW exists for bf16 only).
   // Lane (r, h) holds, for column r of each 32x32 tile, rows
   // gi*8 + h*4 + [0, 4) in acc elements gi*4 .. gi*4+3.
 #pragma unroll
@@ -294,20 +301,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
             const int row = rowbase[a] + gi * 8 + h * 4 + j;
             if (row < g.nrows) orow[row] = acc[a][nb][gi * 4 + j];
           }
-    } else if (MODE == MODE_GATE_UP_RAW) {
-      // the two projections themselves (the backward's recomputation)
-      T *grow = static_cast<T *>(g.out) + (static_cast<int64_t>(m0) + col) * g.out_ld;
-      T *urow = static_cast<T *>(g.out2) + (static_cast<int64_t>(m0) + col) * g.out_ld;
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const int row = rowbase[0] + gi * 8 + h * 4;
-        if (row < g.nrows) {
-          const floatx16 &ga = acc[0][nb];
-          const floatx16 &ua = acc[1][nb];
-          store4<T>(grow + row, ga[gi * 4 + 0], ga[gi * 4 + 1], ga[gi * 4 + 2], ga[gi * 4 + 3]);
-          store4<T>(urow + row, ua[gi * 4 + 0], ua[gi * 4 + 1], ua[gi * 4 + 2], ua[gi * 4 + 3]);
-        }
-      }
     } else if (MODE == MODE_GATE_UP) {
       T *orow = static_cast<T *>(g.out) + (static_cast<int64_t>(m0) + col) * g.out_ld;
 #pragma unroll
