@@ -513,6 +513,9 @@ def main():
         "roofline": roofline,
         "step_hbm_frac": round(alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_mfma_frac": round(alg["step_flops"] / step_s / 1e12 / expert_peak_tf, 4),
+        # max(t_MFMA, t_HBM) / t: the fraction of the step's own roofline
+        "step_roofline_frac": round(max(alg["step_bytes"] / 1e9 / HBM_PEAK_GBS,
+                                        alg["step_flops"] / 1e12 / expert_peak_tf) / step_s, 4),
         "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
         "kernels": kernels,
     }
