@@ -100,10 +100,12 @@ def test_backward_parity(shape):
     compare(run_gpu(cfg, inp, idx, gate, dout, poison=True), ref_backward(cfg, inp, idx, gate, dout))
 
 
-def test_backward_hot_expert_long_k():
-    """One expert takes every token: its wgrad reduces over 700 rows (11
-    K-steps through the three-buffer ring) and its dgrad spans 5 chunks."""
-    T, N, Z = 700, 6, 3
+@pytest.mark.parametrize("T", [700, 1500])
+def test_backward_hot_expert_long_k(T):
+    """One expert takes every token: its wgrad reduces over T rows (11 or
+    24 K-steps through the three-buffer ring) and its dgrad spans 5 or 10
+    chunks (above 8, tiles go in groups of 8 chunks per row block)."""
+    N, Z = 6, 3
     b = np.zeros(N + Z, np.float32)
     b[2] = 10.0
     cfg, inp, idx, gate, dout = case(55, T, 256, 128, N, Z, 3, bias=b)

@@ -149,10 +149,12 @@ def test_z0_and_k_equals_E():
     assert (cnt == cfg.T).all()
 
 
-def test_single_hot_expert_spans_many_chunks():
-    """Bias +10 on FFN expert 3: every token picks it (M_e = T, several
-    128-row chunks), the rest of the slots route normally."""
-    cfg = synth.Config("hot", T=700, d=256, I=128, N=12, Z=4, k=3, dtype="bf16", seed=11)
+@pytest.mark.parametrize("T", [700, 1700])
+def test_single_hot_expert_spans_many_chunks(T):
+    """Bias +10 on FFN expert 3: every token picks it (M_e = T: 5 or 11
+    chunks of 160 rows; above 8 chunks the tiles go in groups of 8 chunks
+    per row block), the rest of the slots route normally."""
+    cfg = synth.Config("hot", T=T, d=256, I=128, N=12, Z=4, k=3, dtype="bf16", seed=11)
     inp = synth.host_inputs(cfg)
     b = inp["bias"].copy()
     b[3] = 10.0
