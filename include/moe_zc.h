@@ -37,6 +37,9 @@
  *     before anything is enqueued; on a validation error nothing is written.
  *     A failed launch returns MOE_ZC_EHIP.  Faults inside kernels surface at
  *     the caller's next synchronisation.
+ *   - Apart from the timer calls, an entry point enqueues kernel launches
+ *     only (no memset, copy or event), so a call with caller-allocated
+ *     buffers can be captured into a HIP graph and replayed.
  */
 #ifndef MOE_ZC_H
 #define MOE_ZC_H
