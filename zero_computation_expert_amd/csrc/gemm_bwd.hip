@@ -20,12 +20,15 @@
 // Every one of these reduces over a dimension that is not contiguous in
 // memory for at least one operand: the weights are stored [K-rows][M] for
 // dgrad (W_down[e] is [d, I] and dgrad reduces over d), and wgrad reduces
-// over rows.  Such an operand is streamed into LDS in its memory layout, 64
-// K-rows x 32 columns per 4 KB sub-tile (64 bytes per row), and the MFMA
-// fragments are read with the gfx950 transposing LDS read
+// over rows.  Such an operand is streamed into LDS in its memory layout and
+// its MFMA fragments are read with the gfx950 transposing LDS read
 // (ds_read_b64_tr_b16), which gives each lane four consecutive K-rows of
-// one column per instruction.  The K-contiguous operands of dgrad (dout,
-// dG/dU, dl rows) use the forward's swizzled 128-byte token tile.
+// one column per instruction.  A wave's own 64 columns (the MN operand) are
+// kept as 64 K-rows x 128 bytes with swizzled 16-byte chunks, so every load
+// is whole lines; the workgroup-shared column operand of wgrad as 4 KB
+// sub-tiles of 64 K-rows x 32 columns (64 bytes per row).  The K-contiguous
+// operands of dgrad (dout, dG/dU, dl rows) use the forward's swizzled
+// 128-byte token tile.
 //
 // Tile structure, streaming and waits follow the forward GEMM: 4 waves, 256
 // output rows per workgroup (two 32-row blocks per wave) x up to 160
