@@ -410,11 +410,253 @@ static int rows_per_wg(int mode) {
   return mode == MODE_GATE_UP || mode == MODE_GATE_UP_RAW ? 128 : 256;
 }
 
+// ---- the 8-wave expert GEMM (bf16 expert modes, 160-token chunks) --------
+// The same tile, LDS layout, ring and waits as gemm_kernel, with two waves
+// per SIMD: waves w and w + 4 share SIMD w % 4 and its 64-row weight group
+// and split the tile's token blocks (waves 0-3 the first ceil(NBR/2), waves
+// 4-7 the rest).  With one wave per SIMD, a tile whose MFMA work is large
+// (hot experts, the dense FFN) stalls on the dependencies inside its wave;
+// the second wave fills them (skewed GATE_UP -7%, dense FFN -8%; prod, bound
+// by the weight stream, unchanged).  Each output element is still produced
+// by one wave with the same MFMA sequence, so results are bit-identical to
+// the 4-wave kernel's.
+
+constexpr int kThreads8 = 512;
+
+// Weight rows: wave (row group rg, half th) loads block a = th (rows
+// th*32 .. +31 of the group: W_gate or W_up for GATE_UP), 4 instructions of
+// 8 rows, with the 4-wave kernel's swizzle.
+template <int AUX>
+__device__ __forceinline__ void load_w8(char *slot_rg, const __amdgpu_buffer_rsrc_t &ra,
+                                        const uint32_t (&wrow)[4], uint32_t wchunk, int wkpos,
+                                        int klen, int ks, int th) {
+  constexpr int KC = 64;
+  const bool ok = ks * KC + wkpos < klen;
+  const uint32_t o = ks * 128 + wchunk;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(slot_rg + (th * 32 + j * 8) * 128), 16,
+                                             ok ? wrow[j] + o : kOOB, 0, 0, AUX);
+#else
+    (void)slot_rg; (void)ra; (void)wrow; (void)o; (void)ok; (void)th;
+#endif
+  }
+}
+
+// Token rows: instruction i of wave w fills tile rows (8i + w)*8 .. +7.
+template <int NBT>
+__device__ __forceinline__ void load_t8(char *tile, const __amdgpu_buffer_rsrc_t &rb,
+                                        const uint32_t (&tvo)[NBT > 0 ? NBT : 1], int wkpos,
+                                        int klen, int ks, int wave) {
+  constexpr int KC = 64;
+  const bool ok = ks * KC + wkpos < klen;
+#pragma unroll
+  for (int i = 0; i < NBT; ++i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (lds_void *)(tile + ((i * 8 + wave) * 8) * kPitch), 16,
+        (ok && tvo[i] != kOOB) ? tvo[i] + ks * 128 : kOOB, 0, 0, 0);
+#else
+    (void)tile; (void)rb; (void)tvo; (void)ok; (void)wave;
+#endif
+  }
+}
+
+template <int NBW>
+__device__ __forceinline__ void compute8w(floatx16 (&acc)[2][NBW > 0 ? NBW : 1],
+                                          const char *slot_rg, const char *tile, int r, int h) {
+  if constexpr (NBW == 0) {
+    (void)acc; (void)slot_rg; (void)tile; (void)r; (void)h;
+  } else {
+    const char *tb = tile + r * kPitch;
+    uint4 A[2][2], B[2][NBW];
+    load_frags<NBW>(A[0], B[0], slot_rg, tb, r, h, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < 3) load_frags<NBW>(A[(q + 1) & 1], B[(q + 1) & 1], slot_rg, tb, r, h, q + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) MfmaOps<bf16_t>::piece(acc[a][nb], A[q & 1][a], B[q & 1][nb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int NBT, int NBW, int S, int AUX>
+__device__ __forceinline__ void kstep8w(int ks, floatx16 (&acc)[2][NBW > 0 ? NBW : 1],
+                                        char *const (&wrg)[3],
+                                        char *const (&tl)[3], const __amdgpu_buffer_rsrc_t &ra,
+                                        const uint32_t (&wrow)[4], uint32_t wchunk, int wkpos,
+                                        const __amdgpu_buffer_rsrc_t &rb,
+                                        const uint32_t (&tvo)[NBT > 0 ? NBT : 1],
+                                        int klen, int nb0, int r, int h, int wave, int th) {
+  load_t8<NBT>(tl[(S + 2) % 3], rb, tvo, wkpos, klen, ks + 2, wave);
+  load_w8<AUX>(wrg[(S + 2) % 3], ra, wrow, wchunk, wkpos, klen, ks + 2, th);
+  asm volatile("" ::: "memory");
+  compute8w<NBW>(acc, wrg[S], tl[S] + nb0 * 32 * kPitch, r, h);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBT + 4));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// one wave's part of a tile: NBR live blocks in the tile, NBW of them this
+// wave's (starting at block nb0)
+template <int MODE, int NBR, int NBW>
+__device__ __forceinline__ void gemm_tile8w(const GemmArgs &g, const TileLoc &t,
+                                            char *const (&s_w)[3], char *const (&tl)[3], int nb0) {
+  // token loads per wave per step: the tile's 4*NBR groups of 8 rows go to
+  // waves g % 8, so waves 0-3 take ceil(NBR/2) and waves 4-7 floor(NBR/2),
+  // the same counts as their token blocks; the highest row is NBR*32 - 1
+  constexpr int NBT = NBW;
+  constexpr uint32_t ES = 2;
+  constexpr int AUX = kStreamOnce;
+  const int e = t.e, rb = t.rb, m0 = t.m0, mcount = t.mcount;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rg = wave & 3, th = wave >> 2;
+  const int r = lane & 31, h = lane >> 5;
+  const int K = g.K;
+  const int klen = t.klen;
+  constexpr bool kGateUp = MODE == MODE_GATE_UP || MODE == MODE_GATE_UP_RAW;
+  const uint32_t wbytes = static_cast<uint32_t>(g.nrows) * static_cast<uint32_t>(K) * ES;
+  int rowbase0;
+  __amdgpu_buffer_rsrc_t ra;
+  int myrow0;  // first weight row this wave loads (block a = th)
+  if (kGateUp) {
+    rowbase0 = rb * 128 + rg * 32;
+    ra = make_rsrc(static_cast<const char *>(th == 0 ? g.wa : g.wb) + e * g.w_expert_stride * ES,
+                   wbytes);
+    myrow0 = rowbase0;
+  } else {
+    rowbase0 = rb * 256 + rg * 64;
+    ra = make_rsrc(static_cast<const char *>(g.wa) + e * g.w_expert_stride * ES, wbytes);
+    myrow0 = rowbase0 + th * 32;
+  }
+  const int lr = lane >> 3;
+  const int chunk = (lane & 7) ^ lr;
+  const uint32_t wchunk = chunk * 16;
+  const int wkpos = chunk * 8;
+  uint32_t wrow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    wrow[j] = static_cast<uint32_t>(min(myrow0 + j * 8 + lr, g.nrows - 1)) * K * ES;
+  __amdgpu_buffer_rsrc_t rbuf;
+  if (kGateUp)
+    rbuf = make_rsrc(g.src, static_cast<uint32_t>(g.T) * K * ES);
+  else
+    rbuf = make_rsrc(static_cast<const char *>(g.src) + static_cast<int64_t>(m0) * K * ES,
+                     static_cast<uint32_t>(mcount) * K * ES);
+  uint32_t tvo[NBT > 0 ? NBT : 1];
+  tvo[0] = kOOB;
+#pragma unroll
+  for (int i = 0; i < NBT; ++i) {
+    const int tr = (i * 8 + wave) * 8 + lr;
+    const uint32_t row = kGateUp ? static_cast<uint32_t>(g.tok[m0 + min(tr, mcount - 1)])
+                                 : static_cast<uint32_t>(tr);
+    tvo[i] = row * K * ES + chunk * 16 + (tr < mcount ? 0u : kOOB);
+  }
+  const int nks = (klen + 63) / 64;
+  char *const wrg[3] = {s_w[0] + rg * kWaveRowBytes, s_w[1] + rg * kWaveRowBytes,
+                        s_w[2] + rg * kWaveRowBytes};
+  constexpr int NBX = NBW > 0 ? NBW : 1;
+  floatx16 acc[2][NBX];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int nb = 0; nb < NBX; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][nb][i] = 0.0f;
+
+  // prologue: steps 0 and 1
+  load_t8<NBT>(tl[0], rbuf, tvo, wkpos, klen, 0, wave);
+  load_w8<AUX>(wrg[0], ra, wrow, wchunk, wkpos, klen, 0, th);
+  asm volatile("" ::: "memory");
+  load_t8<NBT>(tl[1], rbuf, tvo, wkpos, klen, 1, wave);
+  load_w8<AUX>(wrg[1], ra, wrow, wchunk, wkpos, klen, 1, th);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBT + 4));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  int ks = 0;
+  for (; ks + 3 <= nks; ks += 3) {
+    kstep8w<NBT, NBW, 0, AUX>(ks, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, klen, nb0, r, h, wave, th);
+    kstep8w<NBT, NBW, 1, AUX>(ks + 1, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, klen, nb0, r, h, wave, th);
+    kstep8w<NBT, NBW, 2, AUX>(ks + 2, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, klen, nb0, r, h, wave, th);
+  }
+  if (ks < nks)
+    kstep8w<NBT, NBW, 0, AUX>(ks, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, klen, nb0, r, h, wave, th);
+  if (ks + 1 < nks)
+    kstep8w<NBT, NBW, 1, AUX>(ks + 1, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, klen, nb0, r, h, wave, th);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" ::: "memory");
+  // the ring becomes 8 wave-private staging areas of 12 KB (96 rows)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if constexpr (NBW > 0) {
+    char *st;
+    if (wave < 6) st = (wave < 2 ? s_w[0] : (wave < 4 ? s_w[1] : s_w[2])) + (wave & 1) * 12288;
+    else st = wave == 6 ? tl[0] : tl[1];
+    TileLoc ts = t;
+    ts.m0 = t.m0 + nb0 * 32;
+    ts.mcount = max(0, min(t.mcount - nb0 * 32, NBW * 32));
+    stage_epilogue<MODE, NBW>(g.out, g.out2, g.out_ld, g.nrows, ts, acc, st, rowbase0, r, h,
+                              lane);
+  }
+}
+
+template <int MODE, int NBR>
+__device__ __forceinline__ void gemm_tile8(const GemmArgs &g, const TileLoc &t,
+                                           char *const (&s_w)[3], char *const (&tl)[3]) {
+  constexpr int NBW0 = (NBR + 1) / 2, NBW1 = NBR / 2;
+  if ((threadIdx.x >> 6) < 4) gemm_tile8w<MODE, NBR, NBW0>(g, t, s_w, tl, 0);
+  else gemm_tile8w<MODE, NBR, NBW1>(g, t, s_w, tl, NBW0);
+}
+
+template <int MODE, int NB>
+__global__ void __launch_bounds__(kThreads8) gemm8w_kernel(GemmArgs g) {
+  constexpr int MT = NB * 32;
+  __shared__ __attribute__((aligned(16))) char s_w0[kWSlotBytes];
+  __shared__ __attribute__((aligned(16))) char s_w1[kWSlotBytes];
+  __shared__ __attribute__((aligned(16))) char s_w2[kWSlotBytes];
+  __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t0;
+  __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t1;
+  __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t2;
+  const int ntiles = g.meta[0] * g.nrb;
+  const int v = xcd_tile(ntiles);
+  if (v < 0) return;
+  TileLoc t = locate_expert_tile(g, v, MT);
+  const int nb_rt = (t.mcount + 31) / 32;
+  char *const s_w[3] = {s_w0, s_w1, s_w2};
+  char *const tl[3] = {s_t0, s_t1, s_t2};
+  switch (nb_rt) {
+    case 1: gemm_tile8<MODE, 1>(g, t, s_w, tl); break;
+    case 2: gemm_tile8<MODE, 2>(g, t, s_w, tl); break;
+    case 3: gemm_tile8<MODE, 3>(g, t, s_w, tl); break;
+    case 4: gemm_tile8<MODE, 4>(g, t, s_w, tl); break;
+    case 5: if constexpr (NB >= 5) gemm_tile8<MODE, 5>(g, t, s_w, tl); break;
+    default: break;
+  }
+}
+
 template <typename T, int MODE>
 static hipError_t launch_gemm_t(const GemmArgs &g, int nb, int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const int64_t grid = ((max_tiles + 7) / 8) * 8;
   const dim3 gd(static_cast<unsigned>(grid)), bd(kThreads);
+  if constexpr (std::is_same<T, bf16_t>::value && MODE != MODE_ROUTER) {
+    if (nb == 5)  // 160-token chunks: two waves per SIMD
+      hipLaunchKernelGGL((gemm8w_kernel<MODE, 5>), gd, dim3(kThreads8), 0, s, g);
+    else if (nb == 4)
+      hipLaunchKernelGGL((gemm_kernel<T, MODE, 4>), gd, bd, 0, s, g);
+    else
+      hipLaunchKernelGGL((gemm_kernel<T, MODE, 1>), gd, bd, 0, s, g);
+    return hipGetLastError();
+  }
   if (nb == 5)
     hipLaunchKernelGGL((gemm_kernel<T, MODE, 5>), gd, bd, 0, s, g);
   else if (nb == 4)
