@@ -380,7 +380,7 @@ def scmoe_bench(args, cfg, inp, dev):
                    "schedule": best},
         "schedules_ms": {k: round(v, 4) for k, v in ms.items()},
         "overlap_saving": round(1.0 - ms[best] / ms["serial"], 4),
-        "roofline": {"bound": "mfma", "kernel": "dense FFN on gemm_kernel (gate/up + down)",
+        "roofline": {"bound": "mfma", "kernel": "dense FFN on gemm8w_kernel (gate/up + down)",
                      "achieved": round(dense_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dense_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flops_per_call": dense_flops,
@@ -474,8 +474,13 @@ def main():
     peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     expert_peak_tf = MFMA_FP8_PEAK_TFLOPS if args.fp8 else peak_tf
     gu_gbs = alg["gate_up"]["bytes"] / gu_s / 1e9
+    # the library's chunk height: 160 tokens (the 8-wave kernel) when experts
+    # average >= 96 rows, else 128 or 32 (the 4-wave kernel)
+    pmax = cfg.T * min(cfg.k, cfg.N)
+    wide = cfg.N > 0 and pmax // cfg.N >= 96 and cfg.dtype == "bf16"
     kname = ("gemm8_kernel<GATE_UP> (FP8 gate/up GEMM + SwiGLU + [1,128] quantization of H)"
-             if args.fp8 else "gemm_kernel<bf16,GATE_UP> (gate/up GEMM + SwiGLU)")
+             if args.fp8 else ("gemm8w_kernel<bf16,GATE_UP>" if wide else "gemm_kernel<bf16,GATE_UP>")
+             + " (gate/up GEMM + SwiGLU)")
     roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
