@@ -66,9 +66,19 @@ def algorithmic(cfg, counts, fp8=False):
     step_flops = 6 * d * I * P + 2 * d * E * T
     gate_up = {"bytes": touched * 2 * per_expert + T * d * ws, "flops": 4 * d * I * P}
     down = {"bytes": touched * per_expert, "flops": 2 * d * I * P}
-    router = {"bytes": T * d * s + E * d * s, "flops": 2 * d * E * T}
+    # the other stages move each input and output once (fp32 logits, int32
+    # indices, per-16-token-block histograms); their FLOPs are negligible
+    nblk = (T + 15) // 16
+    router = {"bytes": T * d * s + E * d * s + T * E * 4, "flops": 2 * d * E * T}
+    topk = {"bytes": T * E * 4 + E * 4 + T * k * 8 + nblk * E * 4, "flops": 0}
+    scan = {"bytes": 2 * nblk * E * 4 + E * 4 + (cfg.N + 1) * 8, "flops": 0}
+    permute = {"bytes": T * k * 8 + nblk * cfg.N * 4 + P * 4, "flops": 0}
+    if fp8:  # x quantized to E4M3 with one exponent per 128, and the exponents permuted
+        permute["bytes"] += T * d * s + T * d + T * (d // 128) + P * (d // 128)
+    combine = {"bytes": P * d * s + 2 * T * d * s + T * k * 8, "flops": 0}
     return {"P": P, "touched": touched, "step_bytes": step_bytes, "step_flops": step_flops,
-            "gate_up": gate_up, "down": down, "router": router}
+            "gate_up": gate_up, "down": down, "router": router, "topk": topk, "scan": scan,
+            "permute": permute, "combine": combine}
 
 
 def cpu_model():
@@ -469,8 +479,6 @@ def main():
 
     alg = algorithmic(cfg, counts.cpu().numpy(), fp8=args.fp8)
     gu_s = stage_avg["gate_up"] / 1e3
-    dn_s = stage_avg["down"] / 1e3
-    rt_s = stage_avg["router"] / 1e3
     peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     expert_peak_tf = MFMA_FP8_PEAK_TFLOPS if args.fp8 else peak_tf
     gu_gbs = alg["gate_up"]["bytes"] / gu_s / 1e9
@@ -487,15 +495,20 @@ def main():
                 "traffic": measured_traffic(cfg.name, "gemm8" if args.fp8 else "gemm"),
                 "algorithmic_bytes_per_launch": alg["gate_up"]["bytes"],
                 "avg_launch_ms": round(stage_avg["gate_up"], 4)}
+    # every stage against the chip's peaks: HBM bytes for all, MFMA FLOPs for
+    # the three contractions (top-k, the dispatch scans and permute, and
+    # combine have no MFMA work)
     kernels = {}
-    for name, sec in (("router", rt_s), ("gate_up", gu_s), ("down", dn_s)):
+    for name in ("router", "topk", "scan", "permute", "gate_up", "down", "combine"):
+        sec = stage_avg[name] / 1e3
         a = alg[name]
-        pk = peak_tf if name == "router" else expert_peak_tf
         kernels[name] = {"ms": round(sec * 1e3, 4),
                          "GB/s": round(a["bytes"] / sec / 1e9, 1),
-                         "TFLOP/s": round(a["flops"] / sec / 1e12, 1),
-                         "hbm_frac": round(a["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4),
-                         "mfma_frac": round(a["flops"] / sec / 1e12 / pk, 4)}
+                         "hbm_frac": round(a["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4)}
+        if a["flops"]:
+            pk = peak_tf if name == "router" else expert_peak_tf
+            kernels[name]["TFLOP/s"] = round(a["flops"] / sec / 1e12, 1)
+            kernels[name]["mfma_frac"] = round(a["flops"] / sec / 1e12 / pk, 4)
     step_s = ms / 1e3
     res = {
         "metric": METRIC,

@@ -67,35 +67,43 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One step of a DPP maximum over (hi, lo) 64-bit keys: each lane compares
-// its key with the one the DPP control selects (lanes without a source, and
-// lanes outside ROW_MASK, see zero or themselves; 0 is the smallest key).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void dpp_max_step(uint32_t &hi, uint32_t &lo) {
-  const uint32_t h2 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      static_cast<int>(hi), static_cast<int>(hi), CTRL, ROW_MASK, 0xF, true));
-  const uint32_t l2 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      static_cast<int>(lo), static_cast<int>(lo), CTRL, ROW_MASK, 0xF, true));
-  const bool take = h2 > hi || (h2 == hi && l2 > lo);
-  hi = take ? h2 : hi;
-  lo = take ? l2 : lo;
+// Wave reductions by DPP, the result returned to every lane: combines with
+// row_shr 1, 2, 4 and 8 give prefix results within each row of 16 lanes,
+// then the gfx9 row broadcasts (lane 15 of each row into the next row, lane
+// 31 into rows 2 and 3) leave the wave's total in lane 63.  A lane whose DPP
+// source lies outside its row, or whose row the row mask leaves out, combines
+// with ZERO (max of unsigned values, sums) or with itself (float maximum).
+template <int CTRL, int ROW_MASK, bool ZERO>
+__device__ __forceinline__ uint32_t dpp_src(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      ZERO ? 0 : static_cast<int>(v), static_cast<int>(v), CTRL, ROW_MASK, 0xF, ZERO));
 }
 
-// Maximum of a 64-bit key over the (fully active) wave, returned to every
-// lane: prefix maxima within each row of 16 lanes (row_shr 1, 2, 4, 8), then
-// the gfx9 row broadcasts (lane 15 of each row into the next row, lane 31
-// into rows 2 and 3) leave the wave maximum in lane 63.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  uint32_t hi = static_cast<uint32_t>(v >> 32), lo = static_cast<uint32_t>(v);
-  dpp_max_step<0x111, 0xF>(hi, lo);  // row_shr:1
-  dpp_max_step<0x112, 0xF>(hi, lo);  // row_shr:2
-  dpp_max_step<0x114, 0xF>(hi, lo);  // row_shr:4
-  dpp_max_step<0x118, 0xF>(hi, lo);  // row_shr:8
-  dpp_max_step<0x142, 0xA>(hi, lo);  // row_bcast:15
-  dpp_max_step<0x143, 0xC>(hi, lo);  // row_bcast:31
-  hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 63));
-  lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 63));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+template <bool ZERO, typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_dpp(uint32_t v, Op op) {
+  v = op(v, dpp_src<0x111, 0xF, ZERO>(v));  // row_shr:1
+  v = op(v, dpp_src<0x112, 0xF, ZERO>(v));  // row_shr:2
+  v = op(v, dpp_src<0x114, 0xF, ZERO>(v));  // row_shr:4
+  v = op(v, dpp_src<0x118, 0xF, ZERO>(v));  // row_shr:8
+  v = op(v, dpp_src<0x142, 0xA, ZERO>(v));  // row_bcast:15
+  v = op(v, dpp_src<0x143, 0xC, ZERO>(v));  // row_bcast:31
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_dpp<true>(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  return __uint_as_float(wave_reduce_dpp<false>(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  return __uint_as_float(wave_reduce_dpp<true>(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 
 // Router GEMM partition (host side, a pure function of the sizes so that the

@@ -19,10 +19,25 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The two largest keys below fl among a lane's slots (0 where there are none).
+template <int VPL>
+__device__ __forceinline__ void top2_below(const uint64_t (&key)[VPL], uint64_t fl, uint64_t &b1,
+                                           uint64_t &b2) {
+  b1 = 0ull;
+  b2 = 0ull;
+#pragma unroll
+  for (int s = 0; s < VPL; ++s) {
+    const uint64_t x = key[s] < fl ? key[s] : 0ull;
+    const bool top = x > b1;
+    b2 = top ? b1 : (x > b2 ? x : b2);
+    b1 = top ? x : b1;
+  }
+}
+
 // One wave per token.  Expert e lives in lane e % 64, register slot e / 64.
 // Selection key = (ordered score << 32) | (0xffffffff - e): the wave maximum
 // is the highest score and, among equal scores, the lowest index.  Key 0
-// marks a taken or absent expert (every real key is > 0).
+// marks an absent expert (every real key is > 0).
 // The block (kTokPerBlk waves) covers kTokPerBlk consecutive tokens and
 // writes its per-expert selection histogram to blockhist[blockIdx.x].
 template <int VPL>
@@ -79,52 +94,69 @@ __global__ void __launch_bounds__(kTokPerBlk * kWave) topk_kernel(const float *_
         if (e < E) l[s] += lrow[sl * part_stride + e];
       }
     }
+    // softmax: exp through the hardware exp2, one reciprocal of the sum
     float m = l[0];
 #pragma unroll
     for (int s = 1; s < VPL; ++s) m = fmaxf(m, l[s]);
-    m = wave_max(m);
-    float ex[VPL];
+    m = wave_max_dpp(m);
+    float p[VPL];
     float part = 0.0f;
 #pragma unroll
     for (int s = 0; s < VPL; ++s) {
       int e = s * kWave + lane;
-      ex[s] = e < E ? expf(l[s] - m) : 0.0f;
-      part += ex[s];
+      p[s] = e < E ? __builtin_amdgcn_exp2f((l[s] - m) * 1.44269504088896341f) : 0.0f;
+      part += p[s];
     }
-    const float sum = wave_sum(part);
-    float p[VPL];
+    const float inv = __builtin_amdgcn_rcpf(wave_sum_dpp(part));
     uint64_t key[VPL];
 #pragma unroll
     for (int s = 0; s < VPL; ++s) {
       int e = s * kWave + lane;
-      p[s] = ex[s] / sum;
+      p[s] *= inv;
       key[s] = e < E ? (static_cast<uint64_t>(ordered_bits(p[s] + s_bias[e])) << 32) |
                            (0xffffffffu - static_cast<uint32_t>(e))
                      : 0ull;
     }
+    // Selection.  A lane's keys are taken in descending order, so the ones
+    // it still holds are those below the last one it gave up (fl); it keeps
+    // the largest two of them (b1 > b2, 0 = none).  A round takes the wave
+    // maximum of b1: a 32-bit maximum of the score words, and only when
+    // several lanes hold that score, a second one of their index words (the
+    // lowest index wins).  The winning lane moves b2 up; when it has no b2,
+    // every lane recomputes its pair (a uniform branch).
+    uint64_t fl = ~0ull, b1, b2;
+    top2_below<VPL>(key, fl, b1, b2);
     int my_idx = 0;
     float my_gate = 0.0f;
     for (int j = 0; j < k; ++j) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int s = 1; s < VPL; ++s) best = key[s] > best ? key[s] : best;
-      best = wave_max_u64(best);
-      const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
-      const int owner = e & (kWave - 1);
-      const int slot = e / kWave;
-      float pe = 0.0f;
-#pragma unroll
-      for (int s = 0; s < VPL; ++s) {
-        if (s == slot) {
-          pe = p[s];
-          if (lane == owner) key[s] = 0ull;
-        }
+      const uint32_t hi = static_cast<uint32_t>(b1 >> 32), lo = static_cast<uint32_t>(b1);
+      const uint32_t mhi = wave_max_u32(hi);
+      uint64_t win = __ballot(hi == mhi);
+      if (__popcll(win) > 1) {
+        const uint32_t mlo = wave_max_u32(hi == mhi ? lo : 0u);
+        win = __ballot(hi == mhi && lo == mlo);
       }
-      pe = __shfl(pe, owner, kWave);
+      const int owner = __ffsll(static_cast<unsigned long long>(win)) - 1;
+      const int e = static_cast<int>(
+          0xffffffffu - static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), owner)));
+      const int slot = e / kWave;
+      float pe = p[0];
+#pragma unroll
+      for (int s = 1; s < VPL; ++s) pe = s == slot ? p[s] : pe;
+      pe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), owner));
+      if (lane == owner) {
+        fl = b1;
+        b1 = b2;
+        b2 = 0ull;
+      }
       if (lane == j) {
         my_idx = e;
         my_gate = pe;
       }
+      const uint32_t nhi = static_cast<uint32_t>(b1 >> 32), nlo = static_cast<uint32_t>(b1);
+      if ((__builtin_amdgcn_readlane(static_cast<int>(nhi), owner) |
+           __builtin_amdgcn_readlane(static_cast<int>(nlo), owner)) == 0 && j + 1 < k)
+        top2_below<VPL>(key, fl, b1, b2);
     }
     if (lane < k) {
       idx_out[t * k + lane] = my_idx;
@@ -273,6 +305,9 @@ hipError_t launch_topk(const Plan &p, hipStream_t s) {
   if (vpl <= 4)
     hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k, p.idx,
                        p.gate, p.blockhist);
+  else if (vpl <= 12)  // up to 768 experts
+    hipLaunchKernelGGL(topk_kernel<12>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k,
+                       p.idx, p.gate, p.blockhist);
   else if (vpl <= 16)
     hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k,
                        p.idx, p.gate, p.blockhist);
