@@ -23,8 +23,10 @@
  * Expert numbering: 0 .. N-1 are FFN experts, N .. N+Z-1 zero experts.
  *
  * Precision: storage in the dims' dtype (fp32 or bfloat16); products are
- * accumulated in fp32; for bfloat16 the SwiGLU activations and the expert
- * outputs are rounded to bfloat16 between the two expert GEMMs and before
+ * accumulated in fp32; the router softmax is fp32 with the hardware exp2
+ * and reciprocal (a few ulp from exactly rounded); for bfloat16 the SwiGLU
+ * activations and the expert outputs are rounded to bfloat16 between the
+ * two expert GEMMs and before
  * the combine; the combine sums in fp32 in ascending slot order and rounds
  * once.  The combine uses no atomics: results are run-to-run bit-identical.
  *
