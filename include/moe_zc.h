@@ -26,9 +26,9 @@
  * accumulated in fp32; the router softmax is fp32 with the hardware exp2
  * and reciprocal (a few ulp from exactly rounded); for bfloat16 the SwiGLU
  * activations and the expert outputs are rounded to bfloat16 between the
- * two expert GEMMs and before
- * the combine; the combine sums in fp32 in ascending slot order and rounds
- * once.  The combine uses no atomics: results are run-to-run bit-identical.
+ * two expert GEMMs and before the combine; the combine sums in fp32 in
+ * ascending slot order and rounds once.  The combine uses no atomics:
+ * results are run-to-run bit-identical.
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
