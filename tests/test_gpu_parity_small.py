@@ -90,6 +90,34 @@ def test_maximum_expert_count_and_k():
     full_check(cfg, synth.host_inputs(cfg), poison=True)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_exact_ties_go_to_the_lower_index(dt):
+    """Every expert gets the same router row, so all probabilities are bit-equal,
+    and the bias splits the 200 experts into 32 groups (e mod 32) of equal,
+    well separated values.  Selection must take the groups by bias, and within
+    a group ascending expert index: ties between lanes of the top-k kernel
+    (e, e + 32) and between register slots of one lane (e, e + 64), with k
+    reaching into the second group.  The near-tie exclusion of the parity
+    tests does not apply here: the expected indices are exact."""
+    cfg = synth.Config("ties", T=70, d=128, I=64, N=150, Z=50, k=12, dtype=dt, seed=21)
+    inp = synth.host_inputs(cfg)
+    inp["W_router"] = np.ascontiguousarray(np.broadcast_to(inp["W_router"][:1], inp["W_router"].shape))
+    grp = np.random.default_rng(21).permutation(32).astype(np.float32)
+    bias = (grp * np.float32(1e-3))[np.arange(cfg.E) % 32]
+    out, cnt, idx, gate = run_gpu(cfg, inp, bias=bias)
+    want = sorted(range(cfg.E), key=lambda e: (-float(bias[e]), e))[: cfg.k]
+    assert want[0] % 32 == want[6] % 32 != want[7] % 32  # 7 in the top group, then the next
+    assert (idx == np.array(want, np.int32)[None, :]).all()
+    assert (gate == gate[0, 0]).all() and abs(float(gate[0, 0]) - 1.0 / cfg.E) < 1e-6
+    expect_cnt = np.zeros(cfg.E, np.int64)
+    expect_cnt[want] = cfg.T
+    assert (cnt == expect_cnt).all()
+    _, _, _, oprobs = oracle_routing(cfg, inp, bias)
+    ref = P.reference_outputs(cfg, inp, idx, oprobs)
+    err, _ = P.check_outputs(P.out_as_f32(out, dt), ref, dt)
+    print(f"[ties] {dt}: selection exact, rel_frob={err:.3e}", flush=True)
+
+
 def test_deterministic_bitwise():
     cfg = RAGGED[1]
     inp = synth.host_inputs(cfg)
