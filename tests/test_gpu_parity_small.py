@@ -118,6 +118,35 @@ def test_exact_ties_go_to_the_lower_index(dt):
     print(f"[ties] {dt}: selection exact, rel_frob={err:.3e}", flush=True)
 
 
+def test_routing_and_outputs_fuzz():
+    """40 seeded random shapes across the top-k kernel's register layouts (1 to
+    2048 experts: 1 to 32 scores per lane, lanes with no expert, N or Z zero),
+    k from 1 to min(64, E) (k = E included), a bias that dominates the
+    probabilities, none, or one of their size, both dtypes: routing and counts
+    against the oracle (near-tie rule), outputs where FFN experts exist."""
+    rng = np.random.default_rng(1234)
+    seen_k_eq_e = False
+    for i in range(40):
+        E = int(rng.choice([1, 2, 7, 63, 64, 65, 100, 255, 256, 257, 768, 1000, 2048]))
+        N = int(rng.integers(0, E + 1))
+        k = int(rng.integers(1, min(64, E) + 1)) if i % 8 else min(64, E)
+        seen_k_eq_e |= k == E
+        scale = float(rng.choice([0.0, 1e-4, 0.1]))
+        cfg = synth.Config(f"fuzz{i}", T=int(rng.integers(1, 150)), d=int(rng.choice([8, 64, 136])),
+                           I=8, N=N, Z=E - N, k=k, dtype=str(rng.choice(["bf16", "f32"])),
+                           seed=100 + i, bias_lo=-scale, bias_hi=scale)
+        print(f"[fuzz] {cfg}", flush=True)
+        inp = synth.host_inputs(cfg)
+        out, cnt, idx, gate = run_gpu(cfg, inp)
+        oidx, _, omargin, oprobs = oracle_routing(cfg, inp)
+        P.check_routing(cfg, inp["bias"], idx, gate, cnt, oidx, oprobs, omargin)
+        P.check_counts_against_oracle(cfg, idx, cnt, oidx, omargin)
+        if N > 0:
+            ref = P.reference_outputs(cfg, inp, idx, oprobs)
+            P.check_outputs(P.out_as_f32(out, cfg.dtype), ref, cfg.dtype)
+    assert seen_k_eq_e
+
+
 def test_deterministic_bitwise():
     cfg = RAGGED[1]
     inp = synth.host_inputs(cfg)
