@@ -58,6 +58,9 @@ def _load():
         lib.oracle_token_output.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         lib.oracle_combine_given_routing.argtypes = [i64, i32, i32, i32, i32, vp, i32, vp, vp,
                                                      vp, vp, vp, vp]
+        lib.oracle_ffn_pairs.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp]
+        lib.oracle_combine_slots.argtypes = [i64, i32, i32, i32, vp, i32, vp, vp, vp, vp]
+        lib.oracle_ffn_pairs_fp8.argtypes = [i64, i32, i32, i32] + [vp] * 8
         lib.oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, vp, vp]
         f32 = ctypes.c_float
@@ -167,6 +170,65 @@ def combine_given_routing(x, dt, N, idx, gate, w_gate, w_up, w_down) -> np.ndarr
     out = np.empty((T, d), dtype=np.float32)
     _load().oracle_combine_given_routing(T, d, I, N, k, _ptr(x), _DT[dt], _ptr(idx), _ptr(gate),
                                          _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out))
+    return out
+
+
+def _ptr_table(arrays):
+    tab = (ctypes.c_void_p * max(1, len(arrays)))()
+    for i, a in enumerate(arrays):
+        tab[i] = a.ctypes.data
+    return tab
+
+
+def ffn_pairs(x_rows, dt: str, mats) -> np.ndarray:
+    """Expert outputs of (token, FFN expert) pairs: ``x_rows[i]`` is pair i's
+    token row (storage dtype, length d) and ``mats[i] = (W_gate[e], W_up[e],
+    W_down[e])`` its expert's matrices.  Returns y [n, d] fp32, bit-identical
+    to the per-slot expert output inside :func:`token_output`."""
+    n = len(x_rows)
+    rows = [_storage(r, dt) for r in x_rows]
+    mm = [tuple(_storage(a, dt) for a in m) for m in mats]
+    d = rows[0].shape[0] if n else 0
+    I = mm[0][0].shape[0] if n else 1
+    y = np.empty((n, d), dtype=np.float32)
+    if n:
+        _load().oracle_ffn_pairs(n, d, I, _DT[dt], _ptr_table(rows),
+                                 _ptr_table([m[0] for m in mm]), _ptr_table([m[1] for m in mm]),
+                                 _ptr_table([m[2] for m in mm]), _ptr(y))
+    return y
+
+
+def ffn_pairs_fp8(x_rows, dt: str, mats) -> np.ndarray:
+    """As :func:`ffn_pairs` with FP8 experts: ``mats[i] = (qWg, sWg, qWu, sWu,
+    qWd, sWd)`` (E4M3 bytes and fp32 block scales, as from
+    :func:`quantize_fp8` with 128-row blocks); each token row is quantized per
+    [1,128] first.  Bit-identical to one FFN slot of :func:`token_output_fp8`."""
+    n = len(x_rows)
+    rows = [_storage(r, dt) for r in x_rows]
+    mm = [[_c(a, np.uint8 if i % 2 == 0 else np.float32) for i, a in enumerate(m)] for m in mats]
+    d = rows[0].shape[0] if n else 0
+    I = mm[0][0].shape[0] if n else 128
+    y = np.empty((n, d), dtype=np.float32)
+    if n:
+        tabs = [_ptr_table([m[i] for m in mm]) for i in range(6)]
+        _load().oracle_ffn_pairs_fp8(n, d, I, _DT[dt], _ptr_table(rows), *tabs, _ptr(y))
+    return y
+
+
+def combine_slots(x, dt: str, N: int, idx, gate, y_slots) -> np.ndarray:
+    """Steps 4-5 given each FFN slot's expert output ``y_slots`` [T, k, d]
+    (fp32; rows of zero slots are ignored): out = zsum * x + sum_j gate_j *
+    y_j in ascending slot order, the combine of :func:`token_output`."""
+    x = _storage(x, dt)
+    T, d = x.shape
+    idx = _c(idx, np.int32)
+    gate = _c(gate, np.float32)
+    k = idx.shape[1]
+    y_slots = _c(y_slots, np.float32)
+    assert y_slots.shape == (T, k, d)
+    out = np.empty((T, d), dtype=np.float32)
+    _load().oracle_combine_slots(T, d, N, k, _ptr(x), _DT[dt], _ptr(idx), _ptr(gate),
+                                 _ptr(y_slots), _ptr(out))
     return out
 
 

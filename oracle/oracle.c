@@ -207,6 +207,53 @@ void oracle_combine_given_routing(int64_t T, int d, int I, int N, int k, const v
   }
 }
 
+/* Step 3 for a list of (token, FFN expert) pairs: y[i] = Wd (silu(Wg x) *
+ * (Wu x)) for pair i, whose token row x_rows[i] (the inputs' dtype, d
+ * elements) and expert matrices wg[i], wu[i] ([I, d]) and wd[i] ([d, I]) are
+ * given by pointer.  The arithmetic is the per-slot expert of
+ * oracle_token_output, so a check can hold a few experts in memory at a time
+ * and still reproduce that function bit for bit.  y: [n, d] fp32. */
+void oracle_ffn_pairs(int64_t n, int d, int I, int dt, const void *const *x_rows,
+                      const void *const *wg, const void *const *wu, const void *const *wd,
+                      float *y) {
+#pragma omp parallel
+  {
+    float *xf = (float *)malloc(sizeof(float) * (size_t)d);
+    float *h = (float *)malloc(sizeof(float) * (size_t)(I > 0 ? I : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+      for (int c = 0; c < d; ++c) xf[c] = orc_ld(x_rows[i], c, dt);
+      orc_expert(d, I, xf, wg[i], wu[i], wd[i], dt, h, y + i * (int64_t)d);
+    }
+    free(xf);
+    free(h);
+  }
+}
+
+/* Steps 4-5 of [LCF-arch] with the FFN slots' expert outputs given:
+ * out[t] = (sum of zero-slot gates) * x[t] + sum_j gate_j * y[t, j], the FFN
+ * terms added in ascending slot order (the combine of oracle_token_output).
+ * y_slots: [T, k, d] fp32; rows of zero slots (idx >= N) are not read. */
+void oracle_combine_slots(int64_t T, int d, int N, int k, const void *x, int dt,
+                          const int32_t *idx, const float *gate, const float *y_slots,
+                          float *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    const int32_t *it = idx + t * k;
+    const float *gt = gate + t * k;
+    float *o = out + t * (int64_t)d;
+    float zsum = 0.0f;
+    for (int j = 0; j < k; ++j)
+      if (it[j] >= N) zsum += gt[j];
+    for (int i = 0; i < d; ++i) o[i] = zsum * orc_ld(x, t * (int64_t)d + i, dt);
+    for (int j = 0; j < k; ++j) {
+      if (it[j] >= N) continue;
+      const float *y = y_slots + (t * (int64_t)k + j) * (int64_t)d;
+      for (int i = 0; i < d; ++i) o[i] += gt[j] * y[i];
+    }
+  }
+}
+
 /* The whole forward: logits, routing, counts and output (fp32). */
 void oracle_forward(int64_t T, int d, int I, int N, int Z, int k, int dt, const void *x,
                     const void *w_router, const float *bias, const void *w_gate,
@@ -427,6 +474,38 @@ void oracle_token_output_fp8(int d, int I, int N, int k, const void *x_row, int 
   free(qh);
   free(sh);
   free(y);
+}
+
+/* Step 3 with FP8 experts for a list of (token, FFN expert) pairs: pair i's
+ * token row (the inputs' dtype) is quantized per [1,128] and run through its
+ * expert's quantized matrices, exactly as one FFN slot of
+ * oracle_token_output_fp8.  y: [n, d] fp32. */
+void oracle_ffn_pairs_fp8(int64_t n, int d, int I, int dt, const void *const *x_rows,
+                          const uint8_t *const *qwg, const float *const *swg,
+                          const uint8_t *const *qwu, const float *const *swu,
+                          const uint8_t *const *qwd, const float *const *swd, float *y) {
+#pragma omp parallel
+  {
+    float *x = (float *)malloc(sizeof(float) * (size_t)d);
+    uint8_t *qx = (uint8_t *)malloc((size_t)d);
+    float *sx = (float *)malloc(sizeof(float) * (size_t)(d / 128 > 0 ? d / 128 : 1));
+    float *h = (float *)malloc(sizeof(float) * (size_t)(I > 0 ? I : 1));
+    uint8_t *qh = (uint8_t *)malloc((size_t)(I > 0 ? I : 1));
+    float *sh = (float *)malloc(sizeof(float) * (size_t)(I / 128 > 0 ? I / 128 : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+      for (int c = 0; c < d; ++c) x[c] = orc_ld(x_rows[i], c, dt);
+      orc_quant_row(d, x, qx, sx);
+      orc_expert_fp8(d, I, qx, sx, qwg[i], swg[i], qwu[i], swu[i], qwd[i], swd[i], h, qh, sh,
+                     y + i * (int64_t)d);
+    }
+    free(x);
+    free(qx);
+    free(sx);
+    free(h);
+    free(qh);
+    free(sh);
+  }
 }
 
 /* All tokens with given routing; weights q [N, rows, K] with scales

@@ -163,3 +163,20 @@ def test_fp8_approximates_the_unquantized_forward():
     assert (r8["idx"] == r16["idx"]).all()
     err = np.linalg.norm(r8["out"] - r16["out"]) / np.linalg.norm(r16["out"])
     assert 1e-3 < err < 0.1, err
+
+
+def test_ffn_pairs_fp8_and_combine_slots_reproduce_the_fp8_forward():
+    """The expert-major FP8 pieces used at full size give the FP8 forward's
+    outputs bit for bit (same per-row activation quantization, same slot
+    order)."""
+    cfg, inp, w = _fp8_case(seed=34, T=19)
+    qg, sg, qu, su, qd, sd = w
+    r = oracle.forward_fp8(inp["x"], inp["W_router"], inp["bias"], *w, cfg.N, cfg.Z, cfg.k, "bf16")
+    y = np.full((cfg.T, cfg.k, cfg.d), np.nan, np.float32)
+    pairs = [(t, j) for t in range(cfg.T) for j in range(cfg.k) if r["idx"][t, j] < cfg.N]
+    mats = [tuple(a[int(r["idx"][t, j])] for a in (qg, sg, qu, su, qd, sd)) for t, j in pairs]
+    yy = oracle.ffn_pairs_fp8([inp["x"][t] for t, _ in pairs], "bf16", mats)
+    for (t, j), row in zip(pairs, yy):
+        y[t, j] = row
+    out = oracle.combine_slots(inp["x"], "bf16", cfg.N, r["idx"], r["gate"], y)
+    assert np.array_equal(out, r["out"])

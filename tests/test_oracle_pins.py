@@ -304,6 +304,59 @@ def test_token_output_matches_full_forward():
         assert (o == r["out"][t]).all()
 
 
+# ------------------------------------- expert-streamed pieces of the same ---
+def _slot_outputs(cfg, inp, idx, mats_of):
+    """y [T, k, d] of every FFN slot through oracle.ffn_pairs (zero slots NaN,
+    so a combine that read them would not stay finite)."""
+    y = np.full((cfg.T, cfg.k, cfg.d), np.nan, np.float32)
+    pairs = [(t, j) for t in range(cfg.T) for j in range(cfg.k) if idx[t, j] < cfg.N]
+    yy = oracle.ffn_pairs([inp["x"][t] for t, _ in pairs], cfg.dtype,
+                          [mats_of(int(idx[t, j])) for t, j in pairs])
+    for (t, j), row in zip(pairs, yy):
+        y[t, j] = row
+    return y
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ffn_pairs_and_combine_slots_reproduce_the_forward_bit_for_bit(dt):
+    """The expert-major split used by the full-size checks (one expert's
+    matrices in memory at a time) is the same arithmetic as the token-major
+    forward: catches a slot order or a zero-slot term that differs."""
+    cfg = SMALLISH.with_(dtype=dt, T=53)
+    inp = _inputs(cfg)
+    r = oracle.forward(inp["x"], inp["W_router"], inp["bias"], inp["W_gate"], inp["W_up"],
+                       inp["W_down"], cfg.N, cfg.Z, cfg.k, dt)
+    y = _slot_outputs(cfg, inp, r["idx"],
+                      lambda e: (inp["W_gate"][e], inp["W_up"][e], inp["W_down"][e]))
+    out = oracle.combine_slots(inp["x"], dt, cfg.N, r["idx"], r["gate"], y)
+    assert np.array_equal(out, r["out"])
+
+
+def test_combine_slots_matches_float64_formula():
+    """out = (sum of zero-slot gates) x + sum_j gate_j y_j, against a float64
+    evaluation of the formula with arbitrary slot outputs: catches a dropped
+    zero-expert term, a gate applied to the wrong slot or a zero slot's row
+    being read."""
+    rng = np.random.default_rng(5)
+    T, k, d, N = 31, 5, 24, 6
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    idx = np.stack([rng.permutation(N + 4)[:k] for _ in range(T)]).astype(np.int32)
+    gate = rng.random((T, k)).astype(np.float32)
+    y = rng.standard_normal((T, k, d)).astype(np.float32)
+    y[idx >= N] = np.nan
+    got = oracle.combine_slots(x, "f32", N, idx, gate, y)
+    ffn = idx < N
+    g64 = gate.astype(np.float64)
+    zs = np.where(~ffn, g64, 0).sum(1)
+    ref = zs[:, None] * x + np.einsum("tk,tkd->td", np.where(ffn, g64, 0),
+                                      np.where(ffn[..., None], y, 0).astype(np.float64))
+    bound = (k + 2) * U32 * (np.abs(zs)[:, None] * np.abs(x) +
+                             np.einsum("tk,tkd->td", np.where(ffn, g64, 0),
+                                       np.abs(np.where(ffn[..., None], y, 0)))) + 1e-30
+    assert np.isfinite(got).all()
+    assert (np.abs(got - ref) <= bound).all()
+
+
 # -------------------------------------------------- the pages' arithmetic ---
 def test_three_matrix_experts_match_the_activated_parameter_range():
     """The activated-parameter range printed on the page (18.6B .. 31.3B, i.e.
