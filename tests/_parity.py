@@ -7,7 +7,8 @@ different k-th expert.  Such tokens are excluded from the bit-exact index
 and count checks; their outputs are compared against the oracle recomputed
 with the GPU's own choice.  Indices are compared as sets (two experts inside
 the top-k may be near-tied too); the order within a row is only checked to
-be valid (non-increasing oracle score up to 1e-6).
+be valid (non-increasing oracle score up to 1e-6).  In a near-tie row every
+expert the GPU chose must score within 1e-6 of the oracle's k-th choice.
 
 Tolerances: gates 1e-5 absolute; output relative Frobenius error 2e-2 for
 bfloat16 and 1e-5 for fp32 over the compared tokens, and every single token
@@ -56,6 +57,11 @@ def check_routing(cfg, bias, gpu_idx, gpu_gate, gpu_counts, ora_idx, ora_probs, 
     s = ora_probs + bias[None, :]
     sc = np.take_along_axis(s, gi.astype(np.int64), 1)
     assert (np.diff(sc, axis=1) <= MARGIN).all(), "row not ordered by biased score"
+    # near-tie rows: the GPU may swap experts only within the tie, so every
+    # expert it chose scores at least the oracle's k-th score minus MARGIN
+    if near.any():
+        kth = np.take_along_axis(s[near], ora_idx[near][:, -1:].astype(np.int64), 1)
+        assert (sc[near] >= kth - MARGIN).all(), "near-tie row picks an expert outside the tie"
     # gates: the oracle's probability of each GPU-chosen expert
     pg = np.take_along_axis(ora_probs, gi.astype(np.int64), 1)
     gerr = float(np.abs(gg - pg).max()) if gg.size else 0.0

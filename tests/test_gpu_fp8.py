@@ -10,12 +10,14 @@ oracle, while the GPU forward uses the GPU quantizer's output (bit-identical,
 by the first test)."""
 import concurrent.futures as cf
 import os
+import time
 
 import numpy as np
 import pytest
 
 import oracle
 import synth
+from tests import _fullsize as F
 from tests import _parity as P
 
 pytestmark = pytest.mark.gpu
@@ -159,4 +161,45 @@ def test_fp8_prod_full_size_sampled():
     print(f"[fp8] prod sampled {len(rows)} tokens rel_frob={err:.3e} worst_token={worst:.3e}",
           flush=True)
     del dinp, qg, qu, qd
+    torch.cuda.empty_cache()
+
+
+def test_fp8_decode_full_size_every_token():
+    """The decode shape (T=128, d=6144, 512 SwiGLU experts of 2048, 256 zero
+    experts, top-12) with FP8 experts: routing on every token, and the
+    output of every token against the FP8 oracle.  The GPU forward runs on
+    the GPU quantizer's weights (bit-identical to the oracle's, first test);
+    the oracle quantizes each routed expert's bf16 matrices itself, on the
+    host, streaming a few experts at a time."""
+    cfg = synth.DECODE
+    t0 = time.time()
+    log = lambda m: print(f"[fp8 decode] {m} ({time.time() - t0:.0f}s)", flush=True)  # noqa: E731
+    big = cfg.with_(T=cfg.T)
+    dinp = synth.device_inputs(big, DEV)
+    qg, eg = moe.quantize_fp8(dinp["W_gate"], 128)
+    qu, eu = moe.quantize_fp8(dinp["W_up"], 128)
+    qd, ed = moe.quantize_fp8(dinp["W_down"], 128)
+    out, cnt, idx, gate = moe.forward_fp8(dinp["x"], dinp["W_router"], dinp["bias"], qg, eg, qu, eu,
+                                          qd, ed, cfg.N, cfg.Z, cfg.k)
+    torch.cuda.synchronize()
+    del qg, qu, qd, eg, eu, ed
+    out, cnt, idx, gate = P.to_np(out), P.to_np(cnt), P.to_np(idx), P.to_np(gate)
+    x, wr, bias = synth.host_x(cfg), synth.host_router(cfg), synth.host_bias(cfg)
+    assert (x == P.to_np(dinp["x"])).all()
+    logits = oracle.router_logits(x, wr, "bf16")
+    oidx, _, omargin, oprobs = oracle.route_from_logits(logits, bias, cfg.k)
+    info = P.check_routing(cfg, bias, idx, gate, cnt, oidx, oprobs, omargin)
+    P.check_counts_against_oracle(cfg, idx, cnt, oidx, omargin)
+    log(f"routing ok, near_ties={info['near_ties']}, {int((cnt[:cfg.N] > 0).sum())} experts used")
+
+    def fetch(e):
+        mats = [P.to_np(dinp["W_" + w][e]) for w in ("gate", "up", "down")]
+        return tuple(a for m in mats for a in oracle.quantize_fp8(m, "bf16", 128))
+
+    g = np.take_along_axis(oprobs, idx.astype(np.int64), 1).astype(np.float32)
+    ref = F.streamed_reference(x, "bf16", cfg.N, idx, g, np.arange(cfg.T), fetch,
+                               ffn=oracle.ffn_pairs_fp8, log=log)
+    err, worst = P.check_outputs(P.out_as_f32(out, "bf16"), ref, "bf16")
+    log(f"all {cfg.T} tokens rel_frob={err:.3e} worst_token={worst:.3e}")
+    del dinp
     torch.cuda.empty_cache()

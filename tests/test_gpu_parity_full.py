@@ -5,18 +5,21 @@ Inputs are generated on the device by the seeded generator; the host copies
 the oracle reads (x, W_router, bias) are regenerated on the host and checked
 bit-identical to the device ones, and so is one expert per weight tensor.
 Routing (index sets, gates, counts) is checked for EVERY token against the
-oracle; outputs are checked on sampled tokens (the oracle computes them one
-by one), using the sampled tokens' expert matrices copied from the
-generator's device tensors.
+oracle.  Outputs: every token of the small and decode workloads; for prod
+and skewed, a cover of every 32-row block of every expert's permuted rows,
+so every tile of both expert GEMMs (every expert, row block, chunk and
+32-token block, each expert's partial last chunk included) has outputs
+compared.  Expert matrices for the oracle are copied from the generator's
+device tensors, a few experts at a time (tests/_fullsize.py).
 """
-import concurrent.futures as cf
-import os
+import time
 
 import numpy as np
 import pytest
 
 import oracle
 import synth
+from tests import _fullsize as F
 from tests import _parity as P
 
 pytestmark = pytest.mark.gpu
@@ -47,17 +50,14 @@ def device_weights(cfg):
     return inp
 
 
-def _sample_rows(cfg, margin, n):
-    rng = np.random.default_rng(0)
-    rows = set(rng.choice(cfg.T, size=min(n, cfg.T), replace=False).tolist())
-    rows |= {0, cfg.T - 1}
-    rows |= set(np.nonzero(margin < P.MARGIN)[0][:3].tolist())
-    return np.array(sorted(rows))
+def fetch_bf16(dinp):
+    return lambda e: tuple(_np16(dinp["W_" + w][e]) for w in ("gate", "up", "down"))
 
 
-def run_full(cfg, n_sample):
-    print(f"[full] {cfg.name}: T={cfg.T} d={cfg.d} I={cfg.I} N={cfg.N} Z={cfg.Z} k={cfg.k}",
-          flush=True)
+def run_full(cfg, rows_mode):
+    t0 = time.time()
+    log = lambda m: print(f"[full] {cfg.name}: {m} ({time.time() - t0:.0f}s)", flush=True)  # noqa: E731
+    log(f"T={cfg.T} d={cfg.d} I={cfg.I} N={cfg.N} Z={cfg.Z} k={cfg.k}")
     dinp = device_weights(cfg)
     out, cnt, idx, gate = moe.forward(dinp["x"], dinp["W_router"], dinp["bias"], dinp["W_gate"],
                                       dinp["W_up"], dinp["W_down"], cfg.N, cfg.Z, cfg.k)
@@ -76,46 +76,52 @@ def run_full(cfg, n_sample):
     oidx, _, omargin, oprobs = oracle.route_from_logits(logits, bias, cfg.k)
     info = P.check_routing(cfg, bias, idx, gate, cnt, oidx, oprobs, omargin)
     P.check_counts_against_oracle(cfg, idx, cnt, oidx, omargin)
-    print(f"[full] {cfg.name}: routing ok, near_ties={info['near_ties']} "
-          f"gate_err={info['gate_err']:.2e} ffn/token={(idx < cfg.N).sum() / cfg.T:.3f} "
-          f"empty_ffn={(cnt[:cfg.N] == 0).sum()}", flush=True)
+    log(f"routing ok, near_ties={info['near_ties']} gate_err={info['gate_err']:.2e} "
+        f"ffn/token={(idx < cfg.N).sum() / cfg.T:.3f} empty_ffn={(cnt[:cfg.N] == 0).sum()}")
 
-    rows = _sample_rows(cfg, omargin, n_sample)
-
-    def one(t):
-        experts = {}
-        for e in idx[t]:
-            e = int(e)
-            if e < cfg.N:
-                experts[e] = tuple(_np16(dinp["W_" + w][e]) for w in ("gate", "up", "down"))
-        g = oprobs[t, idx[t]].astype(np.float32)
-        return oracle.token_output(x[t], cfg.dtype, cfg.N, idx[t], g, experts)
-
-    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-        ref = np.stack(list(ex.map(one, rows)))
+    if rows_mode == "all":
+        rows, nblocks = np.arange(cfg.T), None
+    else:
+        near = np.nonzero(omargin < P.MARGIN)[0][:8]
+        rows, nblocks = F.block_cover_rows(idx, cfg.N, extra=list(near) + [0, cfg.T - 1])
+    log(f"{len(rows)} tokens to compare" +
+        (f" (cover of {nblocks} 32-row blocks)" if nblocks else " (all)"))
+    # gates: the oracle's probabilities of the experts the GPU chose (equal to
+    # the oracle's own routing outside near-ties)
+    g = np.take_along_axis(oprobs, idx.astype(np.int64), 1).astype(np.float32)
+    ref = F.streamed_reference(x, cfg.dtype, cfg.N, idx, g, rows, fetch_bf16(dinp), log=log)
     got = P.out_as_f32(out[rows], cfg.dtype)
     assert np.isfinite(P.out_as_f32(out, cfg.dtype)).all()
     err, worst = P.check_outputs(got, ref, cfg.dtype)
-    print(f"[full] {cfg.name}: sampled {len(rows)} tokens rel_frob={err:.3e} "
-          f"worst_token={worst:.3e}", flush=True)
-    return cnt, idx
+    log(f"{len(rows)} tokens rel_frob={err:.3e} worst_token={worst:.3e}")
+    return cnt, idx, rows
 
 
 def test_small_full_size():
-    run_full(synth.SMALL, 48)
+    run_full(synth.SMALL, "all")
 
 
 def test_decode_full_size():
-    cnt, idx = run_full(synth.DECODE, 24)
+    cnt, idx, _ = run_full(synth.DECODE, "all")
     assert (cnt[: synth.DECODE.N] == 0).any()  # the decode shape leaves experts empty
 
 
 def test_prod_full_size():
-    run_full(synth.PROD, 16)
+    cnt, idx, rows = run_full(synth.PROD, "cover")
+    # every expert with more than one chunk of 160 rows has its last,
+    # partial chunk covered (by construction of the cover; checked here)
+    tt, _, ee, pos = F.permuted_positions(idx, synth.PROD.N)
+    sel = np.isin(tt, rows)
+    for e in np.nonzero(cnt[: synth.PROD.N] > 160)[0]:
+        assert (pos[sel & (ee == e)] >= (cnt[e] - 1) // 160 * 160).any()
 
 
 def test_skewed_full_size():
-    cnt, _ = run_full(synth.SKEWED, 16)
+    cnt, idx, rows = run_full(synth.SKEWED, "cover")
     assert cnt[0] == synth.SKEWED.T  # the Zipf head expert takes every token
+    # its 103 chunks of 160 rows: every one (and every 32-row block) compared
+    tt, _, ee, pos = F.permuted_positions(idx, synth.SKEWED.N)
+    hot = np.unique(pos[(ee == 0) & np.isin(tt, rows)] // 32)
+    assert hot.size == (synth.SKEWED.T + 31) // 32
     _cache.clear()
     torch.cuda.empty_cache()

@@ -219,6 +219,21 @@ def test_single_hot_expert_spans_many_chunks(T):
     assert cnt[3] == cfg.T and (idx[:, 0] == 3).all()
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_hot_experts_several_row_blocks_and_a_partial_chunk_group(dt):
+    """Two FFN experts take every token (bias +10): each has 1700 rows = 11
+    chunks of 160 (the last one 100 rows), i.e. one full group of 8 chunks
+    per row block and a last, shorter group of 3; d = 640 and I = 384 give 3
+    gate/up row blocks of 128 and 3 down row blocks of 256 (the last one
+    half empty), so the grouped tile order runs over several row blocks."""
+    cfg = synth.Config("hot2", T=1700, d=640, I=384, N=6, Z=3, k=3, dtype=dt, seed=14)
+    inp = synth.host_inputs(cfg)
+    b = inp["bias"].copy()
+    b[[1, 4]] = 10.0
+    _, cnt, idx, _ = full_check(cfg, inp, bias=b)
+    assert cnt[1] == cnt[4] == cfg.T
+
+
 def test_empty_and_single_token():
     cfg = synth.Config("one", T=1, d=64, I=16, N=4, Z=2, k=2, dtype="bf16", seed=12)
     full_check(cfg, synth.host_inputs(cfg))
