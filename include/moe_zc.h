@@ -32,9 +32,10 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library never allocates, frees or synchronises, keeps no mutable global
- *     state, and is re-entrant per stream.  `stream` is a hipStream_t
- *     (NULL = the default stream).
+ *     library never allocates, frees or synchronises, and is re-entrant per
+ *     stream; its only global state is the per-GPU scratch array of
+ *     moe_zc_forward_noalloc (below).  `stream` is a hipStream_t (NULL = the
+ *     default stream).
  *   - Work is enqueued asynchronously on `stream`.  Arguments are validated
  *     before anything is enqueued; on a validation error nothing is written.
  *     A failed launch returns MOE_ZC_EHIP.  Faults inside kernels surface at
@@ -61,7 +62,9 @@ typedef enum {
   MOE_ZC_EDTYPE = -2, /* dtype is neither MOE_ZC_F32 nor MOE_ZC_BF16          */
   MOE_ZC_EALIGN = -3, /* a pointer is misaligned, or d / I not a multiple of 8 */
   MOE_ZC_ENOSPC = -4, /* workspace missing or smaller than the query          */
-  MOE_ZC_EHIP = -5    /* a HIP launch failed                                  */
+  MOE_ZC_EHIP = -5,   /* a HIP launch failed                                  */
+  MOE_ZC_ESCRATCH = -6 /* moe_zc_forward_noalloc: the problem needs more than
+                          MOE_ZC_SCRATCH_BYTES of workspace                   */
 } moe_zc_status;
 
 /* Problem sizes.  Limits: T >= 0; d >= 8 and I >= 8, both multiples of 8;
@@ -101,6 +104,35 @@ int moe_zc_forward(const moe_zc_dims *dims, const void *x, const void *W_router,
                    const float *bias, const void *W_gate, const void *W_up, const void *W_down,
                    void *out, int32_t *counts, int32_t *topk_idx, float *topk_gate,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * The forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results as
+ * moe_zc_forward (bit for bit), except that the workspace is a fixed array
+ * of MOE_ZC_SCRATCH_BYTES inside the library's device image, one per GPU
+ * the library runs on, held until the process ends.  Its address is looked
+ * up once per device (hipGetSymbolAddress, on the first call that targets
+ * the device of `stream`, with that device made current for the lookup);
+ * the call itself allocates nothing.  Nothing in the array needs to start
+ * at zero: a call ignores what the previous one left there.
+ *   - MOE_ZC_ESCRATCH when moe_zc_workspace_bytes(dims) exceeds
+ *     MOE_ZC_SCRATCH_BYTES (e.g. the decode shape T = 128, d = 6144,
+ *     I = 2048, 512 + 256 experts, top-12 needs about 32 MB and fits; the
+ *     prefill shapes do not); other errors as moe_zc_forward; every argument
+ *     is validated before anything is enqueued.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap
+ *     on one GPU (on different streams, or from several threads without
+ *     ordering) race and corrupt each other's results.  Calls on one stream
+ *     are ordered and safe.
+ *   - MOE_ZC_EHIP if the array's address cannot be obtained.
+ * ------------------------------------------------------------------------ */
+#define MOE_ZC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int moe_zc_forward_noalloc(const moe_zc_dims *dims, const void *x, const void *W_router,
+                           const float *bias, const void *W_gate, const void *W_up,
+                           const void *W_down, void *out, int32_t *counts, int32_t *topk_idx,
+                           float *topk_gate, void *stream);
 
 /* Static English text for a status code (never NULL). */
 const char *moe_zc_status_string(int status);

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         s = moe.status_string(code)
         assert s and s != "unknown status"
     assert moe.status_string(42) == "unknown status"
@@ -299,3 +299,28 @@ def test_scmoe_rejects():
     assert sc(ws_moe_bytes=one - 1) == ENOSPC
     assert sc(out_dense=7 * A + 64) == EINVAL    # overlaps out_moe
     assert sc(x_dense=None) == EINVAL
+
+
+@pytest.mark.parametrize("dims,expect", [
+    (D(dtype=7), EDTYPE),
+    (D(k=0), EINVAL),
+    (D(d=100), EALIGN),
+    (D(T=8192, d=6144, I=2048, N=512, Z=256, k=12), -6),  # needs ~1.5 GB > the static scratch
+])
+def test_noalloc_rejects_before_touching_the_device(dims, expect):
+    """moe_zc_forward_noalloc validates like moe_zc_forward and rejects a
+    problem whose workspace exceeds MOE_ZC_SCRATCH_BYTES with its own code,
+    before any HIP call (none can succeed here: there is no GPU)."""
+    st = moe.lib().moe_zc_forward_noalloc(ctypes.byref(dims), A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A,
+                                          7 * A, 8 * A, None, None, None)
+    assert st == expect
+
+
+def test_noalloc_validates_pointers_first():
+    lib = moe.lib()
+    dims = D()
+    assert lib.moe_zc_workspace_bytes(ctypes.byref(dims)) <= moe.SCRATCH_BYTES
+    assert lib.moe_zc_forward_noalloc(ctypes.byref(dims), None, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A,
+                                      7 * A, 8 * A, None, None, None) == EINVAL
+    assert lib.moe_zc_forward_noalloc(ctypes.byref(dims), A + 2, 2 * A, 3 * A, 4 * A, 5 * A,
+                                      6 * A, 7 * A, 8 * A, None, None, None) == EALIGN

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "_moe_zc.so")
 
 F32, BF16 = 0, 1
 STATUS = {0: "MOE_ZC_OK", -1: "MOE_ZC_EINVAL", -2: "MOE_ZC_EDTYPE", -3: "MOE_ZC_EALIGN",
-          -4: "MOE_ZC_ENOSPC", -5: "MOE_ZC_EHIP"}
+          -4: "MOE_ZC_ENOSPC", -5: "MOE_ZC_EHIP", -6: "MOE_ZC_ESCRATCH"}
+SCRATCH_BYTES = 64 << 20  # MOE_ZC_SCRATCH_BYTES: workspace limit of forward_noalloc
 STAGES = ("router", "topk", "scan", "permute", "gate_up", "down", "combine")
 BWD_STAGES = ("route", "router", "recompute", "dgrad_v", "router_bwd", "wgrad_down",
               "wgrad_gate_up", "dgrad_x", "dx", "wgrad_router")
@@ -27,7 +28,8 @@ EXPORTS = ("moe_zc_workspace_bytes", "moe_zc_forward", "moe_zc_status_string",
            "moe_zc_timer_reset", "moe_zc_timer_destroy", "moe_zc_bias_update",
            "moe_zc_quantize_fp8", "moe_zc_workspace_bytes_fp8", "moe_zc_forward_fp8",
            "moe_zc_backward_workspace_bytes", "moe_zc_backward", "moe_zc_dense_workspace_bytes",
-           "moe_zc_dense_ffn", "moe_zc_scmoe_workspace_bytes", "moe_zc_scmoe_forward")
+           "moe_zc_dense_ffn", "moe_zc_scmoe_workspace_bytes", "moe_zc_scmoe_forward",
+           "moe_zc_forward_noalloc")
 
 
 class MoeZcError(RuntimeError):
@@ -59,6 +61,8 @@ def lib():
         fwd = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_zc_forward.restype = ctypes.c_int
         L.moe_zc_forward.argtypes = fwd
+        L.moe_zc_forward_noalloc.restype = ctypes.c_int
+        L.moe_zc_forward_noalloc.argtypes = fwd[:11] + [vp]
         L.moe_zc_forward_timed.restype = ctypes.c_int
         L.moe_zc_forward_timed.argtypes = fwd + [vp]
         L.moe_zc_status_string.restype = ctypes.c_char_p
@@ -209,6 +213,37 @@ def forward(x, W_router, bias, W_gate, W_up, W_down, N: int, Z: int, k: int, *,
     else:
         st = lib().moe_zc_forward_timed(*args, timer.handle)
     _check(st)
+    return out, counts, topk_idx, topk_gate
+
+
+def forward_noalloc(x, W_router, bias, W_gate, W_up, W_down, N: int, Z: int, k: int, *,
+                    out=None, counts=None, topk_idx=None, topk_gate=None, stream=None,
+                    want_routing: bool = True):
+    """Runs moe_zc_forward_noalloc: as :func:`forward`, with the library's
+    static per-GPU scratch array as the workspace (problems needing more than
+    SCRATCH_BYTES of workspace raise MOE_ZC_ESCRATCH).  Output tensors not
+    given are allocated here with torch; the library call itself allocates
+    nothing."""
+    import torch
+
+    T, d = x.shape
+    I = W_gate.shape[1] if (W_gate is not None and N > 0) else 0
+    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x))
+    dev = x.device
+    if out is None:
+        out = torch.empty_like(x)
+    if counts is None:
+        counts = torch.empty(N + Z, dtype=torch.int32, device=dev)
+    if want_routing:
+        if topk_idx is None:
+            topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        if topk_gate is None:
+            topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(lib().moe_zc_forward_noalloc(ctypes.byref(dims), _ptr(x), _ptr(W_router), _ptr(bias),
+                                        _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(out),
+                                        _ptr(counts), _ptr(topk_idx), _ptr(topk_gate), stream))
     return out, counts, topk_idx, topk_gate
 
 

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "moe_zc_internal.h"
@@ -509,7 +510,57 @@ static int dense_impl(int64_t T, int d, int Id, const void *x, const void *w1, c
 
 static int64_t chunk_rows(int64_t T, int nchunks) { return (T + nchunks - 1) / nchunks; }
 
+// ---- the workspace of moe_zc_forward_noalloc --------------------------------
+// A fixed array in this translation unit's device image; every GPU that runs
+// the library gets its own copy at its own address.  In host code the name
+// `noalloc_scratch` is only a stand-in for the symbol: its device address is
+// looked up once per device (hipGetSymbolAddress with that device current)
+// and only that address is ever handed to kernels.
+static __device__ __align__(256) char noalloc_scratch[MOE_ZC_SCRATCH_BYTES];
+
+namespace moezc {
+constexpr int kMaxDevices = 64;
+static std::once_flag g_scratch_once[kMaxDevices];
+static void *g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array (nullptr on failure).
+static void *scratch_of(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return;
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(noalloc_scratch)) == hipSuccess) g_scratch_ptr[dev] = ptr;
+    if (cur != dev) (void)hipSetDevice(cur);
+  });
+  return g_scratch_ptr[dev];
+}
+}  // namespace moezc
+
 extern "C" {
+
+int moe_zc_forward_noalloc(const moe_zc_dims *dims, const void *x, const void *W_router,
+                           const float *bias, const void *W_gate, const void *W_up,
+                           const void *W_down, void *out, int32_t *counts, int32_t *topk_idx,
+                           float *topk_gate, void *stream) {
+  int st;
+  if (!dims_ok(dims, &st)) return st;
+  const size_t need = layout(dims, nullptr, nullptr);
+  if (need > MOE_ZC_SCRATCH_BYTES) return MOE_ZC_ESCRATCH;
+  // every other argument, before the device is touched (a stand-in address
+  // with the scratch array's alignment takes the workspace's place)
+  st = forward_impl(dims, x, W_router, bias, W_gate, W_up, W_down, out, counts, topk_idx,
+                    topk_gate, reinterpret_cast<void *>(uintptr_t(256)), MOE_ZC_SCRATCH_BYTES,
+                    stream, nullptr, nullptr, false);
+  if (st != MOE_ZC_OK) return st;
+  hipDevice_t dev = -1;
+  if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess) return MOE_ZC_EHIP;
+  void *ws = scratch_of(static_cast<int>(dev));
+  if (ws == nullptr) return MOE_ZC_EHIP;
+  return forward_impl(dims, x, W_router, bias, W_gate, W_up, W_down, out, counts, topk_idx,
+                      topk_gate, ws, MOE_ZC_SCRATCH_BYTES, stream, nullptr);
+}
 
 size_t moe_zc_workspace_bytes_fp8(const moe_zc_dims *dims) {
   int st;
@@ -648,6 +699,9 @@ const char *moe_zc_status_string(int status) {
     case MOE_ZC_EALIGN: return "misaligned pointer, or d / I not a multiple of 8";
     case MOE_ZC_ENOSPC: return "workspace missing or too small (or timer full)";
     case MOE_ZC_EHIP: return "HIP launch failed";
+    case MOE_ZC_ESCRATCH:
+      return "problem needs more workspace than the no-alloc entry point's static scratch "
+             "(MOE_ZC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
