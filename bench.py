@@ -81,6 +81,40 @@ def algorithmic(cfg, counts, fp8=False):
             "permute": permute, "combine": combine}
 
 
+def gate_up_kernel_name(cfg, fp8=False):
+    """The kernel the library launches for the gate/up stage of this
+    workload: 160-token chunks (the 8-wave kernel) when experts average at
+    least 96 rows, else 128 or 32 (the 4-wave kernel); fp32 always runs the
+    4-wave kernel."""
+    if fp8:
+        return "gemm8_kernel<GATE_UP> (FP8 gate/up GEMM + SwiGLU + [1,128] quantization of H)"
+    pmax = cfg.T * min(cfg.k, cfg.N)
+    avg = pmax // cfg.N if cfg.N > 0 else 0
+    nb = 5 if avg >= 96 else (4 if avg >= 24 else 1)
+    if cfg.dtype == "bf16":
+        name = "gemm8w_kernel<GATE_UP,5>" if nb == 5 else f"gemm_kernel<bf16,GATE_UP,{nb}>"
+    else:
+        name = f"gemm_kernel<float,GATE_UP,{nb}>"
+    return name + " (gate/up GEMM + SwiGLU)"
+
+
+def dominant_roofline(cfg, work, sec, peak_tf, fp8=False):
+    """Roofline line of the gate/up GEMM, against the bound its algorithmic
+    work binds on: MFMA when its FLOPs at the matrix peak take longer than
+    its bytes at the HBM peak, else HBM."""
+    t_mfma = work["flops"] / (peak_tf * 1e12)
+    t_hbm = work["bytes"] / (HBM_PEAK_GBS * 1e9)
+    base = {"kernel": gate_up_kernel_name(cfg, fp8), "algorithmic_bytes_per_launch": work["bytes"],
+            "algorithmic_flops_per_launch": work["flops"], "avg_launch_ms": round(sec * 1e3, 4)}
+    if t_mfma > t_hbm:
+        tf = work["flops"] / sec / 1e12
+        return {"bound": "mfma", "achieved": round(tf, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(tf / peak_tf, 4), **base}
+    gbs = work["bytes"] / sec / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), **base}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -460,41 +494,55 @@ def main():
     for _ in range(args.warmup):
         fwd(*args_fwd, **kw)
     torch.cuda.synchronize()
-    timer = moe.Timer(max(1, args.steps))
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # headline: exactly `steps` calls back to back, each bracketed by HIP
+    # events on the launch stream (no per-stage events inside); the median
+    # call is the step time
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     ev0.record(stream)
-    for _ in range(args.steps):
-        fwd(*args_fwd, **kw, timer=timer)
+    for a, b in evs:
+        a.record(stream)
+        fwd(*args_fwd, **kw)
+        b.record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
+    calls_ms = [a.elapsed_time(b) for a, b in evs]
+    ms = float(np.median(calls_ms))
+    bracket_ms = ev0.elapsed_time(ev1) / args.steps
+    # per-stage times: a second pass of `steps` calls through the library's
+    # stage timer (HIP events after every kernel group, on the launch stream)
+    timer = moe.Timer(max(1, args.steps))
+    for _ in range(args.steps):
+        fwd(*args_fwd, **kw, timer=timer)
     ncalls, stage_ms = timer.read()
     timer.close()
-    ms = total_ms / args.steps
     stage_avg = {k: v / ncalls for k, v in stage_ms.items()}
-    print(f"[bench] {args.steps} steps: {ms:.3f} ms/step; stages " +
+    # cold: the same call after a 1 GiB write that evicts L2 and the MALL
+    # (256 MB), the scrub outside the events
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold_ms = []
+    for i in range(args.steps):
+        scrub.fill_(i & 0xFF)
+        a, b = evs[i]
+        a.record(stream)
+        fwd(*args_fwd, **kw)
+        b.record(stream)
+    torch.cuda.synchronize()
+    cold_ms = [a.elapsed_time(b) for a, b in evs]
+    del scrub
+    print(f"[bench] {args.steps} steps: median {ms:.3f} ms/step (mean {bracket_ms:.3f}, "
+          f"cold median {float(np.median(cold_ms)):.3f}); stages " +
           " ".join(f"{k}={v:.3f}" for k, v in stage_avg.items()), file=sys.stderr, flush=True)
 
     alg = algorithmic(cfg, counts.cpu().numpy(), fp8=args.fp8)
     gu_s = stage_avg["gate_up"] / 1e3
     peak_tf = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     expert_peak_tf = MFMA_FP8_PEAK_TFLOPS if args.fp8 else peak_tf
-    gu_gbs = alg["gate_up"]["bytes"] / gu_s / 1e9
-    # the library's chunk height: 160 tokens (the 8-wave kernel) when experts
-    # average >= 96 rows, else 128 or 32 (the 4-wave kernel)
-    pmax = cfg.T * min(cfg.k, cfg.N)
-    wide = cfg.N > 0 and pmax // cfg.N >= 96 and cfg.dtype == "bf16"
-    kname = ("gemm8_kernel<GATE_UP> (FP8 gate/up GEMM + SwiGLU + [1,128] quantization of H)"
-             if args.fp8 else ("gemm8w_kernel<bf16,GATE_UP>" if wide else "gemm_kernel<bf16,GATE_UP>")
-             + " (gate/up GEMM + SwiGLU)")
-    roofline = {"bound": "hbm", "kernel": kname,
-                "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(cfg.name, "gemm8" if args.fp8 else "gemm"),
-                "algorithmic_bytes_per_launch": alg["gate_up"]["bytes"],
-                "avg_launch_ms": round(stage_avg["gate_up"], 4)}
+    roofline = dominant_roofline(cfg, alg["gate_up"], gu_s, expert_peak_tf, fp8=args.fp8)
+    roofline["traffic"] = measured_traffic(cfg.name, "gemm8" if args.fp8 else "gemm")
     # every stage against the chip's peaks: HBM bytes for all, MFMA FLOPs for
     # the three contractions (top-k, the dispatch scans and permute, and
     # combine have no MFMA work)
@@ -518,6 +566,12 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "timing": {"ms_per_step": "median of the timed calls (HIP events around each call)",
+                   "mean_ms": round(bracket_ms, 4), "min_ms": round(min(calls_ms), 4),
+                   "max_ms": round(max(calls_ms), 4),
+                   "cold_median_ms": round(float(np.median(cold_ms)), 4),
+                   "cold_tokens_per_s": round(cfg.T / (float(np.median(cold_ms)) / 1e3), 1),
+                   "cold": "each call after a 1 GiB scrub write (L2 and MALL evicted)"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
