@@ -53,7 +53,8 @@ def _load():
         lib = ctypes.CDLL(_SO)
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.oracle_router_logits.argtypes = [i64, i32, i32, vp, vp, i32, vp]
-        lib.oracle_route_from_logits.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp]
+        lib.oracle_route_from_logits.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp,
+                                                 ctypes.c_float]
         lib.oracle_counts.argtypes = [i64, i32, i32, vp, vp]
         lib.oracle_token_output.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         lib.oracle_combine_given_routing.argtypes = [i64, i32, i32, i32, i32, vp, i32, vp, vp,
@@ -62,7 +63,7 @@ def _load():
         lib.oracle_combine_slots.argtypes = [i64, i32, i32, i32, vp, i32, vp, vp, vp, vp]
         lib.oracle_ffn_pairs_fp8.argtypes = [i64, i32, i32, i32] + [vp] * 8
         lib.oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
-                                       vp, vp, vp, vp, vp]
+                                       vp, vp, vp, vp, vp, ctypes.c_float]
         f32 = ctypes.c_float
         lib.oracle_bias_update.argtypes = [i32, i64, vp, vp, vp, vp, f32, f32, f32, f32, i32]
         lib.oracle_e4m3_from_f32.restype = ctypes.c_uint8
@@ -75,10 +76,11 @@ def _load():
         lib.oracle_combine_given_routing_fp8.argtypes = [i64, i32, i32, i32, i32, vp, i32, vp, vp,
                                                          vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_forward_fp8.argtypes = [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
-                                           vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        lib.oracle_token_backward.argtypes = [i32, i32, i32, i32, i32, vp, i32] + [vp] * 13
+                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float]
+        lib.oracle_token_backward.argtypes = [i32, i32, i32, i32, i32, vp, i32] + [vp] * 13 + \
+            [ctypes.c_float]
         lib.oracle_backward.argtypes = [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
-                                        vp, vp, vp, vp, vp, vp, vp, vp]
+                                        vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float]
         lib.oracle_dense_ffn.argtypes = [i64, i32, i32, vp, i32, vp, vp, vp, vp]
         lib.oracle_expert_wgrad_row.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, i32,
                                                 vp, vp, vp]
@@ -107,8 +109,9 @@ def router_logits(x: np.ndarray, w_router: np.ndarray, dt: str) -> np.ndarray:
     return out
 
 
-def route_from_logits(logits: np.ndarray, bias: np.ndarray, k: int):
-    """Returns idx [T,k] int32, gate [T,k] f32, margin [T] f32, probs [T,E] f32."""
+def route_from_logits(logits: np.ndarray, bias: np.ndarray, k: int, routed_scale: float = 1.0):
+    """Returns idx [T,k] int32, gate [T,k] f32 (routed_scale * p of each
+    selected expert), margin [T] f32, probs [T,E] f32 (unscaled)."""
     logits = _c(logits, np.float32)
     bias = _c(bias, np.float32)
     T, E = logits.shape
@@ -117,7 +120,7 @@ def route_from_logits(logits: np.ndarray, bias: np.ndarray, k: int):
     margin = np.empty(T, dtype=np.float32)
     probs = np.empty((T, E), dtype=np.float32)
     _load().oracle_route_from_logits(T, E, k, _ptr(logits), _ptr(bias), _ptr(idx), _ptr(gate),
-                                     _ptr(margin), _ptr(probs))
+                                     _ptr(margin), _ptr(probs), float(routed_scale))
     return idx, gate, margin, probs
 
 
@@ -232,7 +235,8 @@ def combine_slots(x, dt: str, N: int, idx, gate, y_slots) -> np.ndarray:
     return out
 
 
-def forward(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, k: int, dt: str):
+def forward(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, k: int, dt: str,
+            routed_scale: float = 1.0):
     """Whole forward. Returns dict(out, counts, idx, gate, margin)."""
     x = _storage(x, dt)
     w_router = _storage(w_router, dt)
@@ -252,7 +256,7 @@ def forward(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, k: int, dt:
     margin = np.empty(T, dtype=np.float32)
     _load().oracle_forward(T, d, I, N, Z, k, _DT[dt], _ptr(x), _ptr(w_router), _ptr(bias),
                            _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(cnt), _ptr(idx),
-                           _ptr(gate), _ptr(margin))
+                           _ptr(gate), _ptr(margin), float(routed_scale))
     return {"out": out, "counts": cnt, "idx": idx, "gate": gate, "margin": margin}
 
 
@@ -341,7 +345,8 @@ def combine_given_routing_fp8(x, dt, N, idx, gate, qwg, swg, qwu, swu, qwd, swd)
     return out
 
 
-def forward_fp8(x, w_router, bias, qwg, swg, qwu, swu, qwd, swd, N: int, Z: int, k: int, dt: str):
+def forward_fp8(x, w_router, bias, qwg, swg, qwu, swu, qwd, swd, N: int, Z: int, k: int, dt: str,
+                routed_scale: float = 1.0):
     """Whole FP8-expert forward. Returns dict(out, counts, idx, gate, margin)."""
     x = _storage(x, dt)
     w_router = _storage(w_router, dt)
@@ -358,12 +363,13 @@ def forward_fp8(x, w_router, bias, qwg, swg, qwu, swu, qwd, swd, N: int, Z: int,
     margin = np.empty(T, dtype=np.float32)
     _load().oracle_forward_fp8(T, d, I, N, Z, k, _DT[dt], _ptr(x), _ptr(w_router), _ptr(bias),
                                _ptr(qwg), _ptr(swg), _ptr(qwu), _ptr(swu), _ptr(qwd), _ptr(swd),
-                               _ptr(out), _ptr(cnt), _ptr(idx), _ptr(gate), _ptr(margin))
+                               _ptr(out), _ptr(cnt), _ptr(idx), _ptr(gate), _ptr(margin),
+                               float(routed_scale))
     return {"out": out, "counts": cnt, "idx": idx, "gate": gate, "margin": margin}
 
 
 def token_backward(x_row, dt: str, w_router, N: int, idx_row, gate_row, dout_row,
-                   experts: dict) -> dict:
+                   experts: dict, routed_scale: float = 1.0) -> dict:
     """Backward of one token with given routing: dict(dx [d], dgate [k],
     dl [E] (router-logit gradient), h/dg/du [k, I] (rows of FFN slots)).
     ``experts[e] = (W_gate[e], W_up[e], W_down[e])`` for every FFN expert in
@@ -394,15 +400,18 @@ def token_backward(x_row, dt: str, w_router, N: int, idx_row, gate_row, dout_row
     h, dg, du = (np.zeros((k, I), dtype=np.float32) for _ in range(3))
     _load().oracle_token_backward(d, I, N, E, k, _ptr(x_row), _DT[dt], _ptr(w_router),
                                   _ptr(idx_row), _ptr(gate_row), _ptr(dout_row), pg, pu, pd,
-                                  _ptr(dx), _ptr(dgate), _ptr(dl), _ptr(h), _ptr(dg), _ptr(du))
+                                  _ptr(dx), _ptr(dgate), _ptr(dl), _ptr(h), _ptr(dg), _ptr(du),
+                                  float(routed_scale))
     return {"dx": dx, "dgate": dgate, "dl": dl, "h": h, "dg": dg, "du": du}
 
 
 def backward(x, w_router, w_gate, w_up, w_down, idx, gate, dout, N: int, Z: int, dt: str,
-             grads=None) -> dict:
-    """Whole backward with given routing.  Returns dict(dx, dw_router, dw_gate,
-    dw_up, dw_down); the weight gradients are accumulated into ``grads``
-    (a dict of fp32 arrays with those keys) when given, else into zeros."""
+             grads=None, routed_scale: float = 1.0) -> dict:
+    """Whole backward with given routing (gate = routed_scale * p of each
+    selected expert, as the forward gives it).  Returns dict(dx, dw_router,
+    dw_gate, dw_up, dw_down); the weight gradients are accumulated into
+    ``grads`` (a dict of fp32 arrays with those keys) when given, else into
+    zeros."""
     x = _storage(x, dt)
     w_router = _storage(w_router, dt)
     T, d = x.shape
@@ -427,7 +436,7 @@ def backward(x, w_router, w_gate, w_up, w_down, idx, gate, dout, N: int, Z: int,
     _load().oracle_backward(T, d, I, N, Z, k, _DT[dt], _ptr(x), _ptr(w_router), _ptr(w_gate),
                             _ptr(w_up), _ptr(w_down), _ptr(idx), _ptr(gate), _ptr(dout), _ptr(dx),
                             _ptr(g["dw_router"]), _ptr(g["dw_gate"]), _ptr(g["dw_up"]),
-                            _ptr(g["dw_down"]))
+                            _ptr(g["dw_down"]), float(routed_scale))
     out = {"dx": dx}
     out.update(g)
     return out

@@ -79,10 +79,17 @@ static void orc_softmax(int E, const float *l, float *p) {
 
 /* Steps 1-2 of [LCF-arch] from given logits: p = softmax(l); s = p + bias;
  * idx = the k experts of largest s (ties -> lower index), listed by s
- * descending; gate_j = p[idx_j]; margin = s_(k) - s_(k+1) (+inf if k == E).
- * probs (nullable) receives p. */
+ * descending; gate_j = routed_scale * p[idx_j]; margin = s_(k) - s_(k+1)
+ * (+inf if k == E).  probs (nullable) receives p (unscaled).
+ * routed_scale: [LITE] (the LongCat-Flash-Lite article, part 02) fuses the
+ * router's logits, softmax, top-k and a scaling step into one kernel; the
+ * pages do not say what is scaled.  Reading: every selected slot's gate is
+ * multiplied by one constant (FFN and zero slots alike, as the router does
+ * not tell them apart); selection does not depend on it; 1 is the unscaled
+ * method, and multiplying by 1 is exact. */
 void oracle_route_from_logits(int64_t T, int E, int k, const float *logits, const float *bias,
-                              int32_t *idx, float *gate, float *margin, float *probs) {
+                              int32_t *idx, float *gate, float *margin, float *probs,
+                              float routed_scale) {
 #pragma omp parallel
   {
     float *p = (float *)malloc(sizeof(float) * (size_t)E);
@@ -104,7 +111,7 @@ void oracle_route_from_logits(int64_t T, int E, int k, const float *logits, cons
           if (!taken[e] && (best < 0 || s[e] > s[best])) best = e;
         taken[best] = 1;
         idx[t * k + j] = best;
-        gate[t * k + j] = p[best];
+        gate[t * k + j] = routed_scale * p[best];
         last = s[best];
       }
       if (margin) {
@@ -258,11 +265,11 @@ void oracle_combine_slots(int64_t T, int d, int N, int k, const void *x, int dt,
 void oracle_forward(int64_t T, int d, int I, int N, int Z, int k, int dt, const void *x,
                     const void *w_router, const float *bias, const void *w_gate,
                     const void *w_up, const void *w_down, float *out, int32_t *counts,
-                    int32_t *idx, float *gate, float *margin) {
+                    int32_t *idx, float *gate, float *margin, float routed_scale) {
   int E = N + Z;
   float *logits = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * (size_t)E);
   oracle_router_logits(T, d, E, x, w_router, dt, logits);
-  oracle_route_from_logits(T, E, k, logits, bias, idx, gate, margin, NULL);
+  oracle_route_from_logits(T, E, k, logits, bias, idx, gate, margin, NULL, routed_scale);
   oracle_counts(T, k, E, idx, counts);
   oracle_combine_given_routing(T, d, I, N, k, x, dt, idx, gate, w_gate, w_up, w_down, out);
   free(logits);
@@ -555,11 +562,11 @@ void oracle_forward_fp8(int64_t T, int d, int I, int N, int Z, int k, int dt, co
                         const void *w_router, const float *bias, const uint8_t *qwg,
                         const float *swg, const uint8_t *qwu, const float *swu,
                         const uint8_t *qwd, const float *swd, float *out, int32_t *counts,
-                        int32_t *idx, float *gate, float *margin) {
+                        int32_t *idx, float *gate, float *margin, float routed_scale) {
   int E = N + Z;
   float *logits = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * (size_t)E);
   oracle_router_logits(T, d, E, x, w_router, dt, logits);
-  oracle_route_from_logits(T, E, k, logits, bias, idx, gate, margin, NULL);
+  oracle_route_from_logits(T, E, k, logits, bias, idx, gate, margin, NULL, routed_scale);
   oracle_counts(T, k, E, idx, counts);
   oracle_combine_given_routing_fp8(T, d, I, N, k, x, dt, idx, gate, qwg, swg, qwu, swu, qwd, swd,
                                    out);
@@ -581,8 +588,8 @@ void oracle_forward_fp8(int64_t T, int d, int I, int N, int Z, int k, int dt, co
  *     dg = dh u s (1 + g (1 - s));  du = dh g s;
  *     dx += Wg^T dg + Wu^T du;
  *     dWd[e] += (gate_j dout) h^T;  dWg[e] += dg x^T;  dWu[e] += du x^T
- *   router (p = softmax(l), gate_j = p[idx_j]):
- *     dp[e] = dgate_j where idx_j = e, else 0;
+ *   router (p = softmax(l), gate_j = routed_scale * p[idx_j]):
+ *     dp[e] = routed_scale * dgate_j where idx_j = e, else 0;
  *     dl = p * (dp - <p, dp>);  dx += Wr^T dl;  dWr += dl x^T
  * Weight gradients are accumulated into the caller's fp32 arrays.  Every sum
  * runs in ascending index order; weight gradients add tokens in ascending
@@ -596,7 +603,7 @@ void oracle_token_backward(int d, int I, int N, int E, int k, const void *x_row,
                            const void *w_router, const int32_t *idx, const float *gate,
                            const float *dout, const void *const *wg, const void *const *wu,
                            const void *const *wd, float *dx, float *dgate, float *dl,
-                           float *h_s, float *dg_s, float *du_s) {
+                           float *h_s, float *dg_s, float *du_s, float routed_scale) {
   float *x = (float *)malloc(sizeof(float) * (size_t)d);
   float *l = (float *)malloc(sizeof(float) * (size_t)E);
   float *p = (float *)malloc(sizeof(float) * (size_t)E);
@@ -647,7 +654,7 @@ void oracle_token_backward(int d, int I, int N, int E, int k, const void *x_row,
   }
   /* router: softmax backward through the selected gates */
   for (int e = 0; e < E; ++e) dp[e] = 0.0f;
-  for (int j = 0; j < k; ++j) dp[idx[j]] = dgate[j];
+  for (int j = 0; j < k; ++j) dp[idx[j]] = routed_scale * dgate[j]; /* gate_j = scale * p */
   float pdp = 0.0f;
   for (int e = 0; e < E; ++e) pdp += p[e] * dp[e];
   for (int e = 0; e < E; ++e) dl[e] = p[e] * (dp[e] - pdp);
@@ -670,7 +677,7 @@ void oracle_backward(int64_t T, int d, int I, int N, int Z, int k, int dt, const
                      const void *w_router, const void *w_gate, const void *w_up,
                      const void *w_down, const int32_t *idx, const float *gate,
                      const float *dout, float *dx, float *dw_router, float *dw_gate,
-                     float *dw_up, float *dw_down) {
+                     float *dw_up, float *dw_down, float routed_scale) {
   const int E = N + Z;
   const size_t es = dt == ORC_F32 ? 4 : 2;
   const size_t per = (size_t)I * (size_t)d * es;
@@ -698,7 +705,7 @@ void oracle_backward(int64_t T, int d, int I, int N, int Z, int k, int dt, const
       oracle_token_backward(d, I, N, E, k, (const char *)x + (size_t)t * (size_t)d * es, dt,
                             w_router, idx + t * k, gate + t * k, dout + t * (int64_t)d, pg, pu,
                             pd, dx + t * (int64_t)d, dgate + t * k, dl + t * (int64_t)E, h + so,
-                            dg + so, du + so);
+                            dg + so, du + so, routed_scale);
     }
     free(pg);
     free(pu);

@@ -33,8 +33,9 @@ def _f64(a, dt):
     return torch.from_numpy(a.astype(np.float64))
 
 
-def _autograd(cfg, inp, idx, dout):
-    """float64 forward with the routing fixed, differentiated by torch."""
+def _autograd(cfg, inp, idx, dout, scale=1.0):
+    """float64 forward with the routing fixed (gates = scale * p of the
+    selected experts), differentiated by torch."""
     dt = cfg.dtype
     x = _f64(inp["x"], dt).requires_grad_()
     wr = _f64(inp["W_router"], dt).requires_grad_()
@@ -43,7 +44,7 @@ def _autograd(cfg, inp, idx, dout):
     wd = _f64(inp["W_down"], dt).requires_grad_()
     p = torch.softmax(x @ wr.T, dim=1)
     it = torch.from_numpy(idx.astype(np.int64))
-    gate = p.gather(1, it)
+    gate = scale * p.gather(1, it)
     rows = []
     for t in range(cfg.T):
         o = torch.zeros(cfg.d, dtype=torch.float64)
@@ -66,14 +67,17 @@ def _rel(a, b):
     return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_backward_matches_float64_autograd(dt):
+@pytest.mark.parametrize("dt,scale", [("bf16", 1.0), ("f32", 1.0), ("bf16", 2.5)])
+def test_backward_matches_float64_autograd(dt, scale):
+    """With a routed scale s != 1 the gates are s * p, so the router gradient
+    carries s (catches dp = dgate where dp = s * dgate is due)."""
     cfg, inp, fwd, dout = _case(dtype=dt)
     assert (fwd["idx"] >= cfg.N).any() and (fwd["idx"] < cfg.N).any()
+    gate = (np.float32(scale) * fwd["gate"]).astype(np.float32)
     r = oracle.backward(inp["x"], inp["W_router"], inp["W_gate"], inp["W_up"], inp["W_down"],
-                        fwd["idx"], fwd["gate"], synth.bf16_bits_to_f32(dout) if dt == "bf16"
-                        else dout, cfg.N, cfg.Z, dt)
-    ref = _autograd(cfg, inp, fwd["idx"], dout)
+                        fwd["idx"], gate, synth.bf16_bits_to_f32(dout) if dt == "bf16"
+                        else dout, cfg.N, cfg.Z, dt, routed_scale=scale)
+    ref = _autograd(cfg, inp, fwd["idx"], dout, scale)
     for key in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
         err = _rel(r[key], ref[key].numpy())
         assert err < 2e-5, (key, err)

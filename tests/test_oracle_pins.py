@@ -304,6 +304,52 @@ def test_token_output_matches_full_forward():
         assert (o == r["out"][t]).all()
 
 
+# ---------------------------------------------------------- routed scale ---
+def test_routed_scale_of_two_doubles_gates_and_output_exactly():
+    """gate = s * p for every selected slot (FFN and zero), selection
+    unchanged.  With s = 2 every fp32 operation of the combine scales
+    exactly, so the output is exactly twice the unscaled one (catches a scale
+    applied to FFN slots only, or to the selection)."""
+    cfg = SMALLISH.with_(dtype="bf16", T=41)
+    inp = _inputs(cfg)
+    a = (inp["x"], inp["W_router"], inp["bias"], inp["W_gate"], inp["W_up"], inp["W_down"],
+         cfg.N, cfg.Z, cfg.k, "bf16")
+    r1 = oracle.forward(*a)
+    r2 = oracle.forward(*a, routed_scale=2.0)
+    assert (r1["idx"] >= cfg.N).any() and (r1["idx"] < cfg.N).any()
+    assert np.array_equal(r1["idx"], r2["idx"]) and np.array_equal(r1["counts"], r2["counts"])
+    assert np.array_equal(r2["gate"], 2.0 * r1["gate"])
+    assert np.array_equal(r2["out"], 2.0 * r1["out"])
+    assert np.array_equal(oracle.forward(*a, routed_scale=1.0)["out"], r1["out"])
+
+
+def test_routed_scale_matches_float64():
+    """s = 2.5: gates and output against a float64 evaluation with the
+    oracle's own routing."""
+    cfg = SMALLISH.with_(dtype="f32", T=29)
+    inp = _inputs(cfg)
+    s = 2.5
+    r = oracle.forward(inp["x"], inp["W_router"], inp["bias"], inp["W_gate"], inp["W_up"],
+                       inp["W_down"], cfg.N, cfg.Z, cfg.k, "f32", routed_scale=s)
+    x = inp["x"].astype(np.float64)
+    l = x @ inp["W_router"].astype(np.float64).T
+    p = np.exp(l - l.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    g = s * np.take_along_axis(p, r["idx"].astype(np.int64), 1)
+    assert np.abs(r["gate"] - g).max() <= 1e-6 * g.max()
+    ref = np.zeros_like(x)
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            e = int(r["idx"][t, j])
+            if e >= cfg.N:
+                ref[t] += g[t, j] * x[t]
+            else:
+                wg, wu, wd = (inp[w][e].astype(np.float64) for w in ("W_gate", "W_up", "W_down"))
+                gg, uu = wg @ x[t], wu @ x[t]
+                ref[t] += g[t, j] * (wd @ (gg / (1 + np.exp(-gg)) * uu))
+    assert np.linalg.norm(r["out"] - ref) / np.linalg.norm(ref) < 1e-5
+
+
 # ------------------------------------- expert-streamed pieces of the same ---
 def _slot_outputs(cfg, inp, idx, mats_of):
     """y [T, k, d] of every FFN slot through oracle.ffn_pairs (zero slots NaN,
