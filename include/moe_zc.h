@@ -14,7 +14,8 @@
  *      p     = softmax(l)                    (over all E, fp32)
  *   2. s[e]   = p[e] + bias[e]               (selection only)
  *      idx   = the k experts of largest s, by s descending, ties -> lower e
- *      gate_j = p[idx_j]                     (unbiased, no renormalisation)
+ *      gate_j = routed_scale * p[idx_j]      (unbiased, no renormalisation;
+ *                                             routed_scale in moe_zc_dims)
  *   3. FFN expert e < N: y_e = W_down[e] (silu(W_gate[e] x) * (W_up[e] x)),
  *      silu(z) = z / (1 + exp(-z))           (SwiGLU, three matrices, no bias)
  *   4. zero expert e >= N: contributes gate * x (identity)
@@ -67,18 +68,26 @@ typedef enum {
                           MOE_ZC_SCRATCH_BYTES of workspace                   */
 } moe_zc_status;
 
-/* Problem sizes.  Limits: T >= 0; d >= 8 and I >= 8, both multiples of 8;
+/* The problem.  Limits: T >= 0; d >= 8 and I >= 8, both multiples of 8;
  * N >= 0, Z >= 0, 1 <= N + Z <= 2048; 1 <= k <= min(64, N + Z);
  * T * k < 2^31; T * d and I * d (times the element size) below 2 GiB;
- * d and I at most 2^22.  I is ignored when N == 0. */
+ * d and I at most 2^22; routed_scale finite and > 0.  I is ignored when
+ * N == 0.
+ * routed_scale (LongCat-Flash-Lite article, part 02: the fused router kernel
+ * ends with a scaling step; the pages do not say what it scales): every
+ * selected slot's gate is routed_scale * p[idx] (FFN and zero slots alike),
+ * the selection does not depend on it, and the backward's router gradient
+ * carries it.  1.0f is the unscaled method; a zeroed field is rejected
+ * (MOE_ZC_EINVAL) rather than silently zeroing every gate. */
 typedef struct {
-  int64_t T;     /* tokens                                   */
-  int32_t d;     /* model width                               */
-  int32_t I;     /* FFN expert width                          */
-  int32_t N;     /* FFN experts                               */
-  int32_t Z;     /* zero-computation experts                  */
-  int32_t k;     /* experts per token                         */
-  int32_t dtype; /* moe_zc_dtype of x, weights and out        */
+  int64_t T;          /* tokens                                   */
+  int32_t d;          /* model width                               */
+  int32_t I;          /* FFN expert width                          */
+  int32_t N;          /* FFN experts                               */
+  int32_t Z;          /* zero-computation experts                  */
+  int32_t k;          /* experts per token                         */
+  int32_t dtype;      /* moe_zc_dtype of x, weights and out        */
+  float routed_scale; /* gate = routed_scale * p (1.0f: unscaled)  */
 } moe_zc_dims;
 
 /* Bytes of device workspace moe_zc_forward needs for `dims` (worst case:
@@ -96,7 +105,8 @@ size_t moe_zc_workspace_bytes(const moe_zc_dims *dims);
  *   counts     [N+Z]         int32, overwritten (zeroed when T == 0)
  *   topk_idx   [T, k]        int32, nullable; biased score descending,
  *                            ties -> lower index
- *   topk_gate  [T, k]        fp32, nullable; unbiased probabilities
+ *   topk_gate  [T, k]        fp32, nullable; the gates, routed_scale times
+ *                            the unbiased probabilities
  *   workspace  >= moe_zc_workspace_bytes(dims) bytes, 256-byte aligned;
  *              its contents on entry are ignored
  * Returns a moe_zc_status. */
@@ -284,16 +294,17 @@ int moe_zc_scmoe_forward(const moe_zc_dims *dims, int32_t I_dense, int32_t nchun
  *     dg = dh u s (1 + g (1 - s)),  du = dh g s,
  *     dx += W_gate[e]^T dg + W_up[e]^T du,
  *     dW_down[e] += gate_j dout h^T,  dW_gate[e] += dg x^T,  dW_up[e] += du x^T
- *   router (p = softmax(x W_router^T), gate_j = p[idx_j]):
- *     dl = p * (dp - <p, dp>), dp[idx_j] = dgate_j;
+ *   router (p = softmax(x W_router^T), gate_j = routed_scale * p[idx_j]):
+ *     dl = p * (dp - <p, dp>), dp[idx_j] = routed_scale * dgate_j;
  *     dx += W_router^T dl,  dW_router += dl x^T
  *
  *   dims        as for moe_zc_forward; bfloat16 only (MOE_ZC_EDTYPE
  *               otherwise); d and I multiples of 8
  *   x, W_*      the forward's inputs (bfloat16, layouts of moe_zc_forward)
  *   topk_idx    [T, k] int32, topk_gate [T, k] fp32: the forward's routing
- *               outputs.  An entry outside [0, N+Z), or repeating an earlier
- *               expert of its token, is ignored (that slot gets no gradient).
+ *               outputs (with dims->routed_scale as in the forward).  An
+ *               entry outside [0, N+Z), or repeating an earlier expert of
+ *               its token, is ignored (that slot gets no gradient).
  *   dout        [T, d] bfloat16, the gradient of the forward's output
  *   dx          [T, d] bfloat16, overwritten (must not overlap x or dout)
  *   dW_router   [N+Z, d] fp32, dW_gate / dW_up [N, I, d] fp32,

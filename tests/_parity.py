@@ -38,8 +38,10 @@ def out_as_f32(a, dt):
 
 
 def check_routing(cfg, bias, gpu_idx, gpu_gate, gpu_counts, ora_idx, ora_probs, ora_margin,
-                  rows=None):
-    """rows: token indices the oracle arrays refer to (default: all)."""
+                  rows=None, scale=1.0):
+    """rows: token indices the oracle arrays refer to (default: all); scale:
+    the routed scale (gates are scale * p, an fp32 product, as in the
+    oracle)."""
     T = gpu_idx.shape[0]
     rows = np.arange(T) if rows is None else np.asarray(rows)
     gi = gpu_idx[rows]
@@ -63,7 +65,7 @@ def check_routing(cfg, bias, gpu_idx, gpu_gate, gpu_counts, ora_idx, ora_probs, 
         kth = np.take_along_axis(s[near], ora_idx[near][:, -1:].astype(np.int64), 1)
         assert (sc[near] >= kth - MARGIN).all(), "near-tie row picks an expert outside the tie"
     # gates: the oracle's probability of each GPU-chosen expert
-    pg = np.take_along_axis(ora_probs, gi.astype(np.int64), 1)
+    pg = np.float32(scale) * np.take_along_axis(ora_probs, gi.astype(np.int64), 1)
     gerr = float(np.abs(gg - pg).max()) if gg.size else 0.0
     assert gerr <= GATE_TOL, f"gate error {gerr}"
     # counts: bit-exact recount of the GPU's own indices
@@ -109,11 +111,13 @@ def check_outputs(got, ref, dt):
     return agg, worst
 
 
-def reference_outputs(cfg, inp, gpu_idx, ora_probs, rows=None):
+def reference_outputs(cfg, inp, gpu_idx, ora_probs, rows=None, scale=1.0):
     """Oracle outputs for `rows`, routed as the GPU routed them (identical to
-    the oracle's own routing outside near-ties), gates = oracle probabilities."""
+    the oracle's own routing outside near-ties), gates = scale times the
+    oracle probabilities (fp32)."""
     rows = np.arange(gpu_idx.shape[0]) if rows is None else np.asarray(rows)
     idx = gpu_idx[rows]
-    gate = np.take_along_axis(ora_probs, idx.astype(np.int64), 1).astype(np.float32)
+    gate = (np.float32(scale) *
+            np.take_along_axis(ora_probs, idx.astype(np.int64), 1)).astype(np.float32)
     return oracle.combine_given_routing(inp["x"][rows], cfg.dtype, cfg.N, idx, gate,
                                         inp["W_gate"], inp["W_up"], inp["W_down"])

@@ -324,3 +324,10 @@ def test_noalloc_validates_pointers_first():
                                       7 * A, 8 * A, None, None, None) == EINVAL
     assert lib.moe_zc_forward_noalloc(ctypes.byref(dims), A + 2, 2 * A, 3 * A, 4 * A, 5 * A,
                                       6 * A, 7 * A, 8 * A, None, None, None) == EALIGN
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("nan"), float("inf")])
+def test_routed_scale_must_be_finite_and_positive(scale):
+    dims = moe.make_dims(64, 128, 64, 8, 4, 2, moe.BF16, scale)
+    assert moe.lib().moe_zc_workspace_bytes(ctypes.byref(dims)) == 0
+    assert call(dims, ws_bytes=1 << 40) == EINVAL

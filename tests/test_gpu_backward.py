@@ -42,7 +42,7 @@ def case(seed, T, d, I, N, Z, k, bias=None):
     return cfg, inp, idx, gate, synth.host_dout(cfg)
 
 
-def run_gpu(cfg, inp, idx, gate, dout, prior=None, poison=False):
+def run_gpu(cfg, inp, idx, gate, dout, prior=None, poison=False, scale=1.0):
     N = cfg.N
     w = {key: (dev_bf16(inp[key]) if N > 0 else None) for key in ("W_gate", "W_up", "W_down")}
     grads = {}
@@ -56,7 +56,7 @@ def run_gpu(cfg, inp, idx, gate, dout, prior=None, poison=False):
         dev_bf16(inp["x"]), dev_bf16(inp["W_router"]), w["W_gate"], w["W_up"], w["W_down"],
         dev(idx.astype(np.int32)), dev(gate.astype(np.float32)), dev_bf16(dout), N, cfg.Z,
         dW_router=grads.get("dw_router"), dW_gate=grads.get("dw_gate"),
-        dW_up=grads.get("dw_up"), dW_down=grads.get("dw_down"), workspace=ws)
+        dW_up=grads.get("dw_up"), dW_down=grads.get("dw_down"), workspace=ws, routed_scale=scale)
     torch.cuda.synchronize()
     out = {"dx": synth.bf16_bits_to_f32(P.to_np(dx)), "dw_router": P.to_np(dwr)}
     if N > 0:
@@ -64,9 +64,10 @@ def run_gpu(cfg, inp, idx, gate, dout, prior=None, poison=False):
     return out
 
 
-def ref_backward(cfg, inp, idx, gate, dout):
+def ref_backward(cfg, inp, idx, gate, dout, scale=1.0):
     return oracle.backward(inp["x"], inp["W_router"], inp["W_gate"], inp["W_up"], inp["W_down"],
-                           idx, gate, synth.bf16_bits_to_f32(dout), cfg.N, cfg.Z, "bf16")
+                           idx, gate, synth.bf16_bits_to_f32(dout), cfg.N, cfg.Z, "bf16",
+                           routed_scale=scale)
 
 
 def compare(got, ref, keys=("dx", "dw_router", "dw_gate", "dw_up", "dw_down")):
@@ -100,6 +101,17 @@ def test_backward_parity(shape):
     cfg, inp, idx, gate, dout = case(seed, T, d, I, N, Z, k)
     print(f"[bwd] T={T} d={d} I={I} N={N} Z={Z} k={k}", flush=True)
     compare(run_gpu(cfg, inp, idx, gate, dout, poison=True), ref_backward(cfg, inp, idx, gate, dout))
+
+
+def test_backward_routed_scale():
+    """Gates scaled by 2.5 (as the forward with routed_scale 2.5 gives them):
+    the router gradient carries the scale; every gradient against the
+    oracle's backward with the same scale."""
+    s = 2.5
+    cfg, inp, idx, gate, dout = case(62, 200, 256, 192, 12, 6, 4)
+    gs = (np.float32(s) * gate).astype(np.float32)
+    compare(run_gpu(cfg, inp, idx, gs, dout, poison=True, scale=s),
+            ref_backward(cfg, inp, idx, gs, dout, scale=s))
 
 
 @pytest.mark.parametrize("T", [700, 1500])

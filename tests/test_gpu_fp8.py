@@ -59,7 +59,7 @@ def fp8_weights_host(inp):
     return [a for w in ("W_gate", "W_up", "W_down") for a in oracle.quantize_fp8(inp[w], "bf16", 128)]
 
 
-def run_fp8(cfg, inp, qw, bias=None):
+def run_fp8(cfg, inp, qw, bias=None, scale=1.0):
     t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(DEV)
     tu8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     # exponent bytes of the oracle's power-of-two scales
@@ -67,21 +67,22 @@ def run_fp8(cfg, inp, qw, bias=None):
     b = torch.from_numpy(np.ascontiguousarray(inp["bias"] if bias is None else bias)).to(DEV)
     qg, sg, qu, su, qd, sd = qw
     out, cnt, idx, gate = moe.forward_fp8(t16(inp["x"]), t16(inp["W_router"]), b, tu8(qg), ex(sg),
-                                          tu8(qu), ex(su), tu8(qd), ex(sd), cfg.N, cfg.Z, cfg.k)
+                                          tu8(qu), ex(su), tu8(qd), ex(sd), cfg.N, cfg.Z, cfg.k,
+                                          routed_scale=scale)
     torch.cuda.synchronize()
     return P.to_np(out), P.to_np(cnt), P.to_np(idx), P.to_np(gate)
 
 
-def check_fp8(cfg, inp, bias=None):
-    print(f"[fp8] {cfg}", flush=True)
+def check_fp8(cfg, inp, bias=None, scale=1.0):
+    print(f"[fp8] {cfg} routed_scale={scale}", flush=True)
     b = inp["bias"] if bias is None else bias
     qw = fp8_weights_host(inp)
-    out, cnt, idx, gate = run_fp8(cfg, inp, qw, bias=b)
+    out, cnt, idx, gate = run_fp8(cfg, inp, qw, bias=b, scale=scale)
     logits = oracle.router_logits(inp["x"], inp["W_router"], "bf16")
     oidx, _, omargin, oprobs = oracle.route_from_logits(logits, b, cfg.k)
-    info = P.check_routing(cfg, b, idx, gate, cnt, oidx, oprobs, omargin)
+    info = P.check_routing(cfg, b, idx, gate, cnt, oidx, oprobs, omargin, scale=scale)
     P.check_counts_against_oracle(cfg, idx, cnt, oidx, omargin)
-    g = np.take_along_axis(oprobs, idx.astype(np.int64), 1).astype(np.float32)
+    g = (np.float32(scale) * np.take_along_axis(oprobs, idx.astype(np.int64), 1)).astype(np.float32)
     ref = oracle.combine_given_routing_fp8(inp["x"], "bf16", cfg.N, idx, g, *qw)
     got = P.out_as_f32(out, "bf16")
     err, worst = P.check_outputs(got, ref, "bf16")
@@ -101,6 +102,10 @@ FP8_CASES = [
 @pytest.mark.parametrize("cfg", FP8_CASES, ids=lambda c: c.name)
 def test_fp8_forward_parity(cfg):
     check_fp8(cfg, synth.host_inputs(cfg))
+
+
+def test_fp8_routed_scale():
+    check_fp8(FP8_CASES[0], synth.host_inputs(FP8_CASES[0]), scale=1.75)
 
 
 def test_fp8_hot_expert_spans_many_chunks():

@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 moe = pytest.importorskip("zero_computation_expert_amd")
 
 
-def run_gpu(cfg, inp, bias=None, poison=False, **over):
+def run_gpu(cfg, inp, bias=None, poison=False, scale=1.0, **over):
     dev = "cuda:0"
     tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
 
@@ -36,7 +36,7 @@ def run_gpu(cfg, inp, bias=None, poison=False, **over):
     out, cnt, idx, gate = moe.forward(x, dt(inp["W_router"]), b, dt(over.get("W_gate", inp["W_gate"])),
                                       dt(over.get("W_up", inp["W_up"])),
                                       dt(over.get("W_down", inp["W_down"])),
-                                      cfg.N, cfg.Z, cfg.k, workspace=ws)
+                                      cfg.N, cfg.Z, cfg.k, workspace=ws, routed_scale=scale)
     torch.cuda.synchronize()
     assert out.dtype == tdt
     return P.to_np(out), P.to_np(cnt), P.to_np(idx), P.to_np(gate)
@@ -48,14 +48,14 @@ def oracle_routing(cfg, inp, bias=None):
     return oracle.route_from_logits(logits, b, cfg.k)
 
 
-def full_check(cfg, inp, bias=None, poison=False):
-    print(f"[parity] {cfg}", flush=True)
+def full_check(cfg, inp, bias=None, poison=False, scale=1.0):
+    print(f"[parity] {cfg} routed_scale={scale}", flush=True)
     b = inp["bias"] if bias is None else bias
-    out, cnt, idx, gate = run_gpu(cfg, inp, bias=b, poison=poison)
+    out, cnt, idx, gate = run_gpu(cfg, inp, bias=b, poison=poison, scale=scale)
     oidx, ogate, omargin, oprobs = oracle_routing(cfg, inp, b)
-    info = P.check_routing(cfg, b, idx, gate, cnt, oidx, oprobs, omargin)
+    info = P.check_routing(cfg, b, idx, gate, cnt, oidx, oprobs, omargin, scale=scale)
     P.check_counts_against_oracle(cfg, idx, cnt, oidx, omargin)
-    ref = P.reference_outputs(cfg, inp, idx, oprobs)
+    ref = P.reference_outputs(cfg, inp, idx, oprobs, scale=scale)
     got = P.out_as_f32(out, cfg.dtype)
     err, worst = P.check_outputs(got, ref, cfg.dtype)
     print(f"[parity] rel_frob={err:.3e} worst_token={worst:.3e} gate_err={info['gate_err']:.2e} "
@@ -80,6 +80,33 @@ RAGGED = [
 @pytest.mark.parametrize("cfg", RAGGED, ids=lambda c: c.name)
 def test_parity_full(cfg):
     full_check(cfg, synth.host_inputs(cfg), poison=True)
+
+
+@pytest.mark.parametrize("cfg,scale", [(RAGGED[1], 2.5), (RAGGED[2], 2.5), (RAGGED[5], 0.37)],
+                         ids=["bf16-2.5", "f32-2.5", "wide-0.37"])
+def test_routed_scale(cfg, scale):
+    """Gates = routed_scale * p on every slot: routing identical to the
+    unscaled call, gates and outputs against the oracle with the same scale
+    (an FFN-only or selection-side scale would fail the output check)."""
+    inp = synth.host_inputs(cfg)
+    out, cnt, idx, gate = full_check(cfg, inp, poison=True, scale=scale)
+    _, cnt1, idx1, gate1 = run_gpu(cfg, inp)
+    assert np.array_equal(idx, idx1) and np.array_equal(cnt, cnt1)
+    assert np.array_equal(gate, (np.float32(scale) * gate1).astype(np.float32))
+
+
+def test_routed_scale_all_zero_routing():
+    """Every slot on a zero expert: out = (sum of the scaled gates) * x."""
+    cfg = synth.Config("allzero_s", T=70, d=128, I=64, N=6, Z=5, k=4, dtype="f32", seed=15)
+    inp = synth.host_inputs(cfg)
+    b = np.zeros(cfg.E, np.float32)
+    b[cfg.N:] = 10.0
+    out, cnt, idx, gate = run_gpu(cfg, inp, bias=b, scale=3.0)
+    assert (idx >= cfg.N).all()
+    ref = gate.astype(np.float64).sum(1)[:, None] * inp["x"].astype(np.float64)
+    assert P.rel_frob(out, ref) <= P.OUT_TOL["f32"]
+    _, _, _, oprobs = oracle_routing(cfg, inp, b)
+    assert np.abs(gate - 3.0 * np.take_along_axis(oprobs, idx.astype(np.int64), 1)).max() <= 3e-5
 
 
 def test_maximum_expert_count_and_k():

@@ -41,7 +41,7 @@ class MoeZcError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("Z", ctypes.c_int32), ("k", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("routed_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -126,8 +126,8 @@ def _dtype_code(t) -> int:
     return 99  # rejected by the library (MOE_ZC_EDTYPE)
 
 
-def make_dims(T, d, I, N, Z, k, dtype: int) -> Dims:
-    return Dims(int(T), int(d), int(I), int(N), int(Z), int(k), int(dtype))
+def make_dims(T, d, I, N, Z, k, dtype: int, routed_scale: float = 1.0) -> Dims:
+    return Dims(int(T), int(d), int(I), int(N), int(Z), int(k), int(dtype), float(routed_scale))
 
 
 def workspace_bytes(T, d, I, N, Z, k, dtype: int) -> int:
@@ -175,7 +175,8 @@ class Timer:
 
 def forward(x, W_router, bias, W_gate, W_up, W_down, N: int, Z: int, k: int, *,
             out=None, counts=None, topk_idx=None, topk_gate=None, workspace=None,
-            stream=None, timer: Optional[Timer] = None, want_routing: bool = True):
+            stream=None, timer: Optional[Timer] = None, want_routing: bool = True,
+            routed_scale: float = 1.0):
     """Runs moe_zc_forward on torch device tensors.
 
     x [T, d] and the weights share one dtype (float32 or bfloat16); W_gate and
@@ -189,7 +190,7 @@ def forward(x, W_router, bias, W_gate, W_up, W_down, N: int, Z: int, k: int, *,
     T, d = x.shape
     I = W_gate.shape[1] if (W_gate is not None and N > 0) else 0
     dt = _dtype_code(x)
-    dims = make_dims(T, d, I, N, Z, k, dt)
+    dims = make_dims(T, d, I, N, Z, k, dt, routed_scale)
     dev = x.device
     if out is None:
         out = torch.empty_like(x)
@@ -218,7 +219,7 @@ def forward(x, W_router, bias, W_gate, W_up, W_down, N: int, Z: int, k: int, *,
 
 def forward_noalloc(x, W_router, bias, W_gate, W_up, W_down, N: int, Z: int, k: int, *,
                     out=None, counts=None, topk_idx=None, topk_gate=None, stream=None,
-                    want_routing: bool = True):
+                    want_routing: bool = True, routed_scale: float = 1.0):
     """Runs moe_zc_forward_noalloc: as :func:`forward`, with the library's
     static per-GPU scratch array as the workspace (problems needing more than
     SCRATCH_BYTES of workspace raise MOE_ZC_ESCRATCH).  Output tensors not
@@ -228,7 +229,7 @@ def forward_noalloc(x, W_router, bias, W_gate, W_up, W_down, N: int, Z: int, k: 
 
     T, d = x.shape
     I = W_gate.shape[1] if (W_gate is not None and N > 0) else 0
-    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x))
+    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x), routed_scale)
     dev = x.device
     if out is None:
         out = torch.empty_like(x)
@@ -294,7 +295,7 @@ def workspace_bytes_fp8(T, d, I, N, Z, k) -> int:
 def forward_fp8(x, W_router, bias, W_gate, W_gate_exp, W_up, W_up_exp, W_down, W_down_exp,
                 N: int, Z: int, k: int, *, out=None, counts=None, topk_idx=None, topk_gate=None,
                 workspace=None, stream=None, timer: Optional[Timer] = None,
-                want_routing: bool = True):
+                want_routing: bool = True, routed_scale: float = 1.0):
     """moe_zc_forward_fp8 on torch device tensors: x, W_router bfloat16; the
     expert matrices E4M3 bytes (uint8) with E8M0 exponents as returned by
     quantize_fp8(W, 128).  Returns (out, counts, topk_idx, topk_gate)."""
@@ -302,7 +303,7 @@ def forward_fp8(x, W_router, bias, W_gate, W_gate_exp, W_up, W_up_exp, W_down, W
 
     T, d = x.shape
     I = W_gate.shape[1] if (W_gate is not None and N > 0) else 0
-    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x))
+    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x), routed_scale)
     dev = x.device
     if out is None:
         out = torch.empty_like(x)
@@ -338,7 +339,7 @@ def backward_workspace_bytes(T, d, I, N, Z, k) -> int:
 
 def backward(x, W_router, W_gate, W_up, W_down, topk_idx, topk_gate, dout, N: int, Z: int, *,
              dx=None, dW_router=None, dW_gate=None, dW_up=None, dW_down=None, workspace=None,
-             stream=None, timer: Optional[Timer] = None):
+             stream=None, timer: Optional[Timer] = None, routed_scale: float = 1.0):
     """moe_zc_backward on torch device tensors (bfloat16 x, weights and dout;
     the forward's topk_idx int32 / topk_gate float32).  Returns (dx, dW_router,
     dW_gate, dW_up, dW_down); the float32 weight gradients are accumulated
@@ -348,7 +349,7 @@ def backward(x, W_router, W_gate, W_up, W_down, topk_idx, topk_gate, dout, N: in
     T, d = x.shape
     k = topk_idx.shape[1]
     I = W_gate.shape[1] if (W_gate is not None and N > 0) else 0
-    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x))
+    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x), routed_scale)
     dev = x.device
     if dx is None:
         dx = torch.empty_like(x)
@@ -414,7 +415,7 @@ def scmoe_workspace_bytes(T, d, I, N, Z, k, I_dense, nchunks):
 def scmoe_forward(x_moe, W_router, bias, W_gate, W_up, W_down, x_dense, W1, W3, W2, N: int,
                   Z: int, k: int, nchunks: int, stream_moe, stream_dense, *, out_moe=None,
                   out_dense=None, counts=None, topk_idx=None, topk_gate=None, ws_moe=None,
-                  ws_dense=None):
+                  ws_dense=None, routed_scale: float = 1.0):
     """moe_zc_scmoe_forward: the MoE over x_moe (nchunks token chunks) on
     stream_moe and the dense FFN over x_dense on stream_dense (torch streams
     or raw handles).  Returns (out_moe, out_dense, counts [nchunks, N+Z],
@@ -425,7 +426,7 @@ def scmoe_forward(x_moe, W_router, bias, W_gate, W_up, W_down, x_dense, W1, W3, 
     I = W_gate.shape[1] if (W_gate is not None and N > 0) else 0
     Id = W1.shape[0]
     dev = x_moe.device
-    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x_moe))
+    dims = make_dims(T, d, I, N, Z, k, _dtype_code(x_moe), routed_scale)
     if out_moe is None:
         out_moe = torch.empty_like(x_moe)
     if out_dense is None:

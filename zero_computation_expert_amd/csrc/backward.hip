@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(kTokPerBlk * kWave) router_bwd_kernel(
     int k, const int32_t *__restrict__ idx_s, const int32_t *__restrict__ rowmap,
     const float *__restrict__ dpart, int nrbi, int64_t dpart_stride,
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dout, int d, bf16_t *__restrict__ dl,
-    int ldl) {
+    int ldl, float routed_scale) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlk + threadIdx.x / kWave;
   if (t >= T) return;
@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(kTokPerBlk * kWave) router_bwd_kernel(
     if (ej >= 0 && (ej & (kWave - 1)) == lane) {
 #pragma unroll
       for (int s = 0; s < VPL; ++s)
-        if (s == ej / kWave) dp[s] = gj;
+        if (s == ej / kWave) dp[s] = routed_scale * gj;  // gate = routed_scale * p
     }
   }
   float pd = 0.0f;
@@ -237,7 +237,7 @@ hipError_t launch_router_bwd(const Plan &p, hipStream_t s) {
 #define MOEZC_RB_ARGS                                                                    \
   p.logits, p.rs.split, p.T * p.E, p.T, p.E, p.N, p.k, p.idx, p.rowmap, p.dpart, nrbi, \
       p.pmax, static_cast<const bf16_t *>(p.x), static_cast<const bf16_t *>(p.dout), p.d, \
-      static_cast<bf16_t *>(p.dl), p.ldl
+      static_cast<bf16_t *>(p.dl), p.ldl, p.routed_scale
   const dim3 grid(p.nblk), block(kTokPerBlk * kWave);
   if (vpl <= 4)
     hipLaunchKernelGGL(router_bwd_kernel<4>, grid, block, 0, s, MOEZC_RB_ARGS);

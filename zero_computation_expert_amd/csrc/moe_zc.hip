@@ -25,7 +25,8 @@ static bool dims_ok(const moe_zc_dims *dm, int *status) {
   const int64_t E = static_cast<int64_t>(dm->N) + dm->Z;
   if (dm->T < 0 || dm->N < 0 || dm->Z < 0 || E < 1 || E > kMaxE || dm->k < 1 || dm->k > E ||
       dm->k > kMaxK || dm->d < 8 || (dm->N > 0 && dm->I < 8) ||
-      dm->T * static_cast<int64_t>(dm->k) >= (int64_t(1) << 31)) {
+      dm->T * static_cast<int64_t>(dm->k) >= (int64_t(1) << 31) ||
+      !(dm->routed_scale > 0.0f && dm->routed_scale <= 3.4028234e38f)) {
     *status = MOE_ZC_EINVAL;
     return false;
   }
@@ -185,6 +186,7 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   p.Z = dm->Z;
   p.E = dm->N + dm->Z;
   p.k = dm->k;
+  p.routed_scale = dm->routed_scale;
   p.dtype = dm->dtype;
   p.nblk = static_cast<int>((T + kTokPerBlk - 1) / kTokPerBlk);
   p.pmax = T * std::min(dm->k, dm->N);
@@ -379,6 +381,7 @@ static int backward_impl(const moe_zc_dims *dm, const void *x, const void *w_rou
   p.Z = dm->Z;
   p.E = dm->N + dm->Z;
   p.k = dm->k;
+  p.routed_scale = dm->routed_scale;
   p.dtype = MOE_ZC_BF16;
   p.nblk = static_cast<int>((T + kTokPerBlk - 1) / kTokPerBlk);
   p.pmax = T * std::min(dm->k, dm->N);
@@ -493,6 +496,7 @@ static int dense_impl(int64_t T, int d, int Id, const void *x, const void *w1, c
   p.N = 1;
   p.E = 1;
   p.k = 1;
+  p.routed_scale = 1.0f;
   p.dtype = MOE_ZC_BF16;
   p.pmax = T;
   p.nbmax = T >= 96 ? 5 : (T >= 24 ? 4 : 1);

@@ -172,6 +172,7 @@ struct Plan {
   int nblk;   // ceil(T / kTokPerBlk)
   int64_t pmax;  // T * min(k, N): upper bound of (token, FFN expert) pairs
   int nbmax;  // 32-token column blocks per GEMM chunk (1, 4 or 5)
+  float routed_scale;  // gate = routed_scale * p (1 for the dense FFN)
   RouterSplit rs;  // router GEMM partition
   // caller tensors
   const void *x, *w_router, *w_gate, *w_up, *w_down;

@@ -8,7 +8,10 @@
 // scores to hold the FFN / zero selection ratio; the per-expert selection
 // counts are what the bias controller consumes.  Softmax over all experts,
 // the bias used for selection only, unbiased gates and the tie-break towards
-// the lower expert index are this library's readings of that passage.
+// the lower expert index are this library's readings of that passage.  The
+// gates are scaled by the routed scale (LongCat-Flash-Lite article, part 02:
+// the fused router kernel ends with a scaling step; the reading is that every
+// selected slot's gate is multiplied by one constant).
 #include "moe_zc_internal.h"
 
 namespace moezc {
@@ -46,7 +49,8 @@ __global__ void __launch_bounds__(kTokPerBlk * kWave) topk_kernel(const float *_
                                                    const float *__restrict__ bias, int64_t T,
                                                    int E, int k, int32_t *__restrict__ idx_out,
                                                    float *__restrict__ gate_out,
-                                                   int32_t *__restrict__ blockhist) {
+                                                   int32_t *__restrict__ blockhist,
+                                                   float routed_scale) {
   __shared__ float s_bias[kMaxE];
   __shared__ int s_hist[kMaxE];
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -160,7 +164,7 @@ __global__ void __launch_bounds__(kTokPerBlk * kWave) topk_kernel(const float *_
     }
     if (lane < k) {
       idx_out[t * k + lane] = my_idx;
-      gate_out[t * k + lane] = my_gate;
+      gate_out[t * k + lane] = routed_scale * my_gate;
       atomicAdd(&s_hist[my_idx], 1);
     }
   }
@@ -304,16 +308,16 @@ hipError_t launch_topk(const Plan &p, hipStream_t s) {
   int vpl = (p.E + kWave - 1) / kWave;
   if (vpl <= 4)
     hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k, p.idx,
-                       p.gate, p.blockhist);
+                       p.gate, p.blockhist, p.routed_scale);
   else if (vpl <= 12)  // up to 768 experts
     hipLaunchKernelGGL(topk_kernel<12>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k,
-                       p.idx, p.gate, p.blockhist);
+                       p.idx, p.gate, p.blockhist, p.routed_scale);
   else if (vpl <= 16)
     hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k,
-                       p.idx, p.gate, p.blockhist);
+                       p.idx, p.gate, p.blockhist, p.routed_scale);
   else
     hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k,
-                       p.idx, p.gate, p.blockhist);
+                       p.idx, p.gate, p.blockhist, p.routed_scale);
   return hipGetLastError();
 }
 
