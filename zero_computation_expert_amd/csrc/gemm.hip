@@ -77,11 +77,12 @@ struct MfmaOps<float> {
 
 // Fragments of 16-byte piece q: the wave's two weight fragments (swizzled
 // slot) and the NBR token fragments (swizzled tile); both operands hold
-// logical chunk h*4 + q of a row whose low 3 bits are r's.
+// logical chunk h*4 + q of a row whose bits 0-4 are r's (lds_swz reads bits
+// 1-3 only).
 template <int NBR>
 __device__ __forceinline__ void load_frags(uint4 (&A)[2], uint4 (&B)[NBR], const char *slot_wave,
                                            const char *tb, int r, int h, int q) {
-  const int chunk = ((h * 4 + q) ^ (r & 7)) * 16;
+  const int chunk = ((h * 4 + q) ^ lds_swz(r)) * 16;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
     A[a] = *reinterpret_cast<const uint4 *>(slot_wave + (a * 32 + r) * 128 + chunk);
@@ -92,7 +93,8 @@ __device__ __forceinline__ void load_frags(uint4 (&A)[2], uint4 (&B)[NBR], const
 
 // Token rows of one K-step, gathered straight into LDS: instruction i of
 // wave w fills tile rows (4i + w)*8 .. +7, lane (row lr, position p) loading
-// logical chunk p ^ lr of its row (the swizzle the fragment reads expect).
+// logical chunk p ^ lds_swz(row) of its row (the swizzle the fragment reads
+// expect; bit 3 of those rows is w's bit 0, so the chunk is fixed per lane).
 // Rows past the chunk's end and steps past K read zeros (kOOB offset); the
 // instruction is issued regardless, so every step issues exactly NBR token
 // loads.
@@ -100,7 +102,7 @@ template <typename T, int NBR>
 __device__ __forceinline__ void load_t(char *tile, const uint32_t (&tvo)[NBR],
                                        const TileState<NBR> &st, int ks, int wave) {
   constexpr int KC = 128 / sizeof(T);
-  const bool ok = ks * KC + st.wkpos < st.K;
+  const bool ok = ks * KC + st.tkpos < st.K;
 #pragma unroll
   for (int i = 0; i < NBR; ++i) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -198,10 +200,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileLoc &t,
     st.ra[0] = st.ra[1] =
         make_rsrc(static_cast<const char *>(g.wa) + e * g.w_expert_stride * ES, wbytes);
   }
-  const int lr = lane >> 3;           // row within an 8-row group
-  const int chunk = (lane & 7) ^ lr;  // logical 16-byte chunk this lane loads
-  st.wchunk = chunk * 16;
-  st.wkpos = chunk * (16 / static_cast<int>(ES));
+  const int lr = lane >> 3;  // row within an 8-row group
+  // logical 16-byte chunk this lane loads: weight rows of an 8-row group
+  // with bit 3 clear (par 0) or set (par 1); token rows of this wave's groups
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int c = (lane & 7) ^ lds_swz(par * 8 + lr);
+    st.wchunk[par] = c * 16;
+    st.wkpos[par] = c * (16 / static_cast<int>(ES));
+  }
+  const int chunk = (lane & 7) ^ lds_swz((wave & 1) * 8 + lr);
+  st.tkpos = chunk * (16 / static_cast<int>(ES));
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -425,21 +434,22 @@ constexpr int kThreads8 = 512;
 
 // Weight rows: wave (row group rg, half th) loads block a = th (rows
 // th*32 .. +31 of the group: W_gate or W_up for GATE_UP), 4 instructions of
-// 8 rows, with the 4-wave kernel's swizzle.
+// 8 rows, with the 4-wave kernel's swizzle (instruction j's rows have bit 3
+// equal to j's bit 0: chunk offset wchunk[j & 1]).
 template <int AUX>
 __device__ __forceinline__ void load_w8(char *slot_rg, const __amdgpu_buffer_rsrc_t &ra,
-                                        const uint32_t (&wrow)[4], uint32_t wchunk, int wkpos,
-                                        int klen, int ks, int th) {
+                                        const uint32_t (&wrow)[4], const uint32_t (&wchunk)[2],
+                                        const int (&wkpos)[2], int klen, int ks, int th) {
   constexpr int KC = 64;
-  const bool ok = ks * KC + wkpos < klen;
-  const uint32_t o = ks * 128 + wchunk;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    const bool ok = ks * KC + wkpos[j & 1] < klen;
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(slot_rg + (th * 32 + j * 8) * 128), 16,
-                                             ok ? wrow[j] + o : kOOB, 0, 0, AUX);
+                                             ok ? wrow[j] + ks * 128 + wchunk[j & 1] : kOOB, 0, 0,
+                                             AUX);
 #else
-    (void)slot_rg; (void)ra; (void)wrow; (void)o; (void)ok; (void)th;
+    (void)slot_rg; (void)ra; (void)wrow; (void)ok; (void)th; (void)wchunk;
 #endif
   }
 }
@@ -447,10 +457,10 @@ __device__ __forceinline__ void load_w8(char *slot_rg, const __amdgpu_buffer_rsr
 // Token rows: instruction i of wave w fills tile rows (8i + w)*8 .. +7.
 template <int NBT>
 __device__ __forceinline__ void load_t8(char *tile, const __amdgpu_buffer_rsrc_t &rb,
-                                        const uint32_t (&tvo)[NBT > 0 ? NBT : 1], int wkpos,
+                                        const uint32_t (&tvo)[NBT > 0 ? NBT : 1], int tkpos,
                                         int klen, int ks, int wave) {
   constexpr int KC = 64;
-  const bool ok = ks * KC + wkpos < klen;
+  const bool ok = ks * KC + tkpos < klen;
 #pragma unroll
   for (int i = 0; i < NBT; ++i) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -489,11 +499,11 @@ template <int NBT, int NBW, int S, int AUX>
 __device__ __forceinline__ void kstep8w(int ks, floatx16 (&acc)[2][NBW > 0 ? NBW : 1],
                                         char *const (&wrg)[3],
                                         char *const (&tl)[3], const __amdgpu_buffer_rsrc_t &ra,
-                                        const uint32_t (&wrow)[4], uint32_t wchunk, int wkpos,
-                                        const __amdgpu_buffer_rsrc_t &rb,
-                                        const uint32_t (&tvo)[NBT > 0 ? NBT : 1],
+                                        const uint32_t (&wrow)[4], const uint32_t (&wchunk)[2],
+                                        const int (&wkpos)[2], const __amdgpu_buffer_rsrc_t &rb,
+                                        const uint32_t (&tvo)[NBT > 0 ? NBT : 1], int tkpos,
                                         int klen, int nb0, int r, int h, int wave, int th) {
-  load_t8<NBT>(tl[(S + 2) % 3], rb, tvo, wkpos, klen, ks + 2, wave);
+  load_t8<NBT>(tl[(S + 2) % 3], rb, tvo, tkpos, klen, ks + 2, wave);
   load_w8<AUX>(wrg[(S + 2) % 3], ra, wrow, wchunk, wkpos, klen, ks + 2, th);
   asm volatile("" ::: "memory");
   compute8w<NBW>(acc, wrg[S], tl[S] + nb0 * 32 * kPitch, r, h);
@@ -537,9 +547,17 @@ __device__ __forceinline__ void gemm_tile8w(const GemmArgs &g, const TileLoc &t,
     myrow0 = rowbase0 + th * 32;
   }
   const int lr = lane >> 3;
-  const int chunk = (lane & 7) ^ lr;
-  const uint32_t wchunk = chunk * 16;
-  const int wkpos = chunk * 8;
+  uint32_t wchunk[2];
+  int wkpos[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int c = (lane & 7) ^ lds_swz(par * 8 + lr);
+    wchunk[par] = c * 16;
+    wkpos[par] = c * 8;
+  }
+  // token rows (i*8 + wave)*8 + lr: bit 3 is wave's bit 0
+  const int chunk = (lane & 7) ^ lds_swz((wave & 1) * 8 + lr);
+  const int tkpos = chunk * 8;
   uint32_t wrow[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -572,10 +590,10 @@ __device__ __forceinline__ void gemm_tile8w(const GemmArgs &g, const TileLoc &t,
       for (int i = 0; i < 16; ++i) acc[a][nb][i] = 0.0f;
 
   // prologue: steps 0 and 1
-  load_t8<NBT>(tl[0], rbuf, tvo, wkpos, klen, 0, wave);
+  load_t8<NBT>(tl[0], rbuf, tvo, tkpos, klen, 0, wave);
   load_w8<AUX>(wrg[0], ra, wrow, wchunk, wkpos, klen, 0, th);
   asm volatile("" ::: "memory");
-  load_t8<NBT>(tl[1], rbuf, tvo, wkpos, klen, 1, wave);
+  load_t8<NBT>(tl[1], rbuf, tvo, tkpos, klen, 1, wave);
   load_w8<AUX>(wrg[1], ra, wrow, wchunk, wkpos, klen, 1, th);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBT + 4));
@@ -584,14 +602,14 @@ __device__ __forceinline__ void gemm_tile8w(const GemmArgs &g, const TileLoc &t,
   asm volatile("" ::: "memory");
   int ks = 0;
   for (; ks + 3 <= nks; ks += 3) {
-    kstep8w<NBT, NBW, 0, AUX>(ks, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, klen, nb0, r, h, wave, th);
-    kstep8w<NBT, NBW, 1, AUX>(ks + 1, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, klen, nb0, r, h, wave, th);
-    kstep8w<NBT, NBW, 2, AUX>(ks + 2, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, klen, nb0, r, h, wave, th);
+    kstep8w<NBT, NBW, 0, AUX>(ks, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, tkpos, klen, nb0, r, h, wave, th);
+    kstep8w<NBT, NBW, 1, AUX>(ks + 1, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, tkpos, klen, nb0, r, h, wave, th);
+    kstep8w<NBT, NBW, 2, AUX>(ks + 2, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, tkpos, klen, nb0, r, h, wave, th);
   }
   if (ks < nks)
-    kstep8w<NBT, NBW, 0, AUX>(ks, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, klen, nb0, r, h, wave, th);
+    kstep8w<NBT, NBW, 0, AUX>(ks, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, tkpos, klen, nb0, r, h, wave, th);
   if (ks + 1 < nks)
-    kstep8w<NBT, NBW, 1, AUX>(ks + 1, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, klen, nb0, r, h, wave, th);
+    kstep8w<NBT, NBW, 1, AUX>(ks + 1, acc, wrg, tl, ra, wrow, wchunk, wkpos, rbuf, tvo, tkpos, klen, nb0, r, h, wave, th);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   asm volatile("" ::: "memory");
   // the ring becomes 8 wave-private staging areas of 12 KB (96 rows)

@@ -93,6 +93,18 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t rs, uint32_t off) 
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// XOR swizzle of the 16-byte chunks of a 128-byte LDS row (bf16 / fp32
+// expert GEMMs): logical chunk c of row `row` sits at chunk c ^ lds_swz(row).
+// The LDS serves a 16-byte read to 16 lanes per clock over 64 four-byte
+// banks; a 128-byte row covers half of them, so the bank group of a chunk is
+// (row & 1) * 8 + physical chunk.  The MFMA fragment reads hand lanes 0-15
+// rows 0-15 (and so on), all at one logical chunk: with the swizzle taken
+// from row bits 1-3, the even rows and the odd rows of any 16 consecutive
+// rows each land on 8 distinct chunks, so the 16 lanes hit 16 distinct bank
+// groups.  (Swizzling by row bits 0-2 put rows r and r + 8 on the same
+// banks: half of all LDS cycles of the expert GEMMs were bank conflicts.)
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
+
 // Per-thread state of one tile.
 template <int NB>
 struct TileState {
@@ -100,8 +112,10 @@ struct TileState {
   __amdgpu_buffer_rsrc_t rb;     // token rows (B operand)
   uint32_t wrow[2][4];           // byte offset of the weight row this lane loads in each
                                  // direct-to-LDS instruction (block, 8-row group)
-  uint32_t wchunk;               // byte offset of the 16-byte chunk this lane loads
-  int wkpos;                     // K element of that chunk within a step
+  uint32_t wchunk[2];            // byte offset of the 16-byte chunk this lane loads, for
+                                 // 8-row groups with row bit 3 clear / set
+  int wkpos[2];                  // K element of that chunk within a step
+  int tkpos;                     // K element of this lane's token chunk (direct-to-LDS)
   uint32_t vob[NB];              // byte offset of this thread's token row piece (or kOOB)
   int kpos_b;                    // K element of this thread's token piece within a step
   int K;
@@ -110,16 +124,17 @@ struct TileState {
 // Weights of K-step ks from HBM into this wave's LDS slot: 8 fully
 // coalesced instructions of 8 rows x 128 bytes.  Lane l of instruction i
 // loads row (i%4)*8 + l/8 of block i/4 and lands in LDS chunk l%8, which
-// therefore holds the row's 16-byte chunk (l%8) ^ (l/8) (XOR swizzle).
+// therefore holds the row's 16-byte chunk given by the layout's swizzle
+// (wchunk; the bf16 / fp32 GEMMs use lds_swz, the FP8 GEMMs (l%8) ^ (l/8)).
 // Chunks past K read zeros.
 template <typename T, int NB, int AUX>
 __device__ __forceinline__ void load_w(char *slot_wave, const TileState<NB> &st, int ks) {
   constexpr int KC = 128 / sizeof(T);
-  const bool ok = ks * KC + st.wkpos < st.K;
-  const uint32_t o = ks * 128 + st.wchunk;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int a = i >> 2;
+    const bool ok = ks * KC + st.wkpos[i & 1] < st.K;  // rows of instruction i: bit 3 = i & 1
+    const uint32_t o = ks * 128 + st.wchunk[i & 1];
 #if defined(__HIP_DEVICE_COMPILE__)  // the direct-to-LDS load exists only for the device
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         st.ra[a], (lds_void *)(slot_wave + (a * 32 + (i & 3) * 8) * 128), 16,

@@ -175,9 +175,9 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
   }
   {
     const int lr = lane >> 3;
-    const int chunk = (lane & 7) ^ lr;
-    st.wchunk = chunk * 16;
-    st.wkpos = chunk * 16;
+    const int chunk = (lane & 7) ^ lr;  // this kernel's swizzle: row bits 0-2
+    st.wchunk[0] = st.wchunk[1] = chunk * 16;
+    st.wkpos[0] = st.wkpos[1] = chunk * 16;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
