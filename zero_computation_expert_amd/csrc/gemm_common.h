@@ -93,8 +93,9 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t rs, uint32_t off) 
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// XOR swizzle of the 16-byte chunks of a 128-byte LDS row (bf16 / fp32
-// expert GEMMs): logical chunk c of row `row` sits at chunk c ^ lds_swz(row).
+// XOR swizzle of the 16-byte chunks of a 128-byte LDS row (the expert
+// GEMMs' weight slots and token tiles): logical chunk c of row `row` sits at
+// chunk c ^ lds_swz(row).
 // The LDS serves a 16-byte read to 16 lanes per clock over 64 four-byte
 // banks; a 128-byte row covers half of them, so the bank group of a chunk is
 // (row & 1) * 8 + physical chunk.  The MFMA fragment reads hand lanes 0-15
@@ -124,8 +125,7 @@ struct TileState {
 // Weights of K-step ks from HBM into this wave's LDS slot: 8 fully
 // coalesced instructions of 8 rows x 128 bytes.  Lane l of instruction i
 // loads row (i%4)*8 + l/8 of block i/4 and lands in LDS chunk l%8, which
-// therefore holds the row's 16-byte chunk given by the layout's swizzle
-// (wchunk; the bf16 / fp32 GEMMs use lds_swz, the FP8 GEMMs (l%8) ^ (l/8)).
+// therefore holds the row's 16-byte chunk (l%8) ^ lds_swz(row) (wchunk).
 // Chunks past K read zeros.
 template <typename T, int NB, int AUX>
 __device__ __forceinline__ void load_w(char *slot_wave, const TileState<NB> &st, int ks) {
@@ -158,11 +158,11 @@ __device__ __forceinline__ void load_b(uint4 (&xr)[NB], const TileState<NB> &st,
     xr[i] = bload(st.rb, (ok && st.vob[i] != kOOB) ? st.vob[i] + ks * 128 : kOOB);
 }
 
-// Token piece bp of tile row brow + 32 i lands in chunk bp ^ (brow & 7) of
-// that row (the row's low 3 bits are brow's: 32 i is a multiple of 8).
+// Token piece bp of tile row brow + 32 i lands in chunk bp ^ lds_swz(brow)
+// of that row (the row's bits 1-3 are brow's: 32 i is a multiple of 32).
 template <int NB>
 __device__ __forceinline__ void store_b(char *tile, const uint4 (&xr)[NB], int brow, int bp) {
-  const int chunk = (bp ^ (brow & 7)) * 16;
+  const int chunk = (bp ^ lds_swz(brow)) * 16;
 #pragma unroll
   for (int i = 0; i < NB; ++i)
     *reinterpret_cast<uint4 *>(tile + (brow + 32 * i) * kPitch + chunk) = xr[i];

@@ -15,7 +15,7 @@
 // the same byte, which scales the whole step) and accumulate in fp32.
 //
 // Everything else is the bf16 design of gemm.hip (direct-to-LDS weight ring,
-// register-staged swizzled token tile, explicit waits, XCD-aware tile order,
+// register-staged token tile, the same LDS swizzle, explicit waits, XCD-aware tile order,
 // per-count tile bodies): per step the bytes moved and read from LDS are the
 // same as bf16's, for twice the K.  A tile's exponents (its token rows' and
 // its weight blocks' rows, K/128 bytes each) are copied into LDS once, in
@@ -48,13 +48,13 @@ __device__ __forceinline__ void mfma8(floatx16 &acc, const Frag8 &a, const Frag8
 
 // Fragments of MFMA m of a step (m = 0, 1): lane (r, h) holds the logical
 // 16-byte chunks 4m + 2h and 4m + 2h + 1 of its row (the same K elements for
-// A and B, so the dot products pair the right bytes), read from the
-// XOR-swizzled weight slot and token tile.
+// A and B, so the dot products pair the right bytes), read from the weight
+// slot and token tile, both swizzled by lds_swz (conflict-free reads).
 template <int NBR>
 __device__ __forceinline__ void load_frags8(Frag8 (&A)[2], Frag8 (&B)[NBR], const char *slot_wave,
                                             const char *tb, int r, int h, int m) {
   const int c0 = 4 * m + 2 * h;
-  const int p0 = (c0 ^ (r & 7)) * 16, p1 = ((c0 + 1) ^ (r & 7)) * 16;
+  const int p0 = (c0 ^ lds_swz(r)) * 16, p1 = ((c0 + 1) ^ lds_swz(r)) * 16;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     A[a].lo = *reinterpret_cast<const uint4 *>(slot_wave + (a * 32 + r) * 128 + p0);
@@ -175,9 +175,12 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
   }
   {
     const int lr = lane >> 3;
-    const int chunk = (lane & 7) ^ lr;  // this kernel's swizzle: row bits 0-2
-    st.wchunk[0] = st.wchunk[1] = chunk * 16;
-    st.wkpos[0] = st.wkpos[1] = chunk * 16;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {  // 8-row groups with row bit 3 clear / set
+      const int c = (lane & 7) ^ lds_swz(par * 8 + lr);
+      st.wchunk[par] = c * 16;
+      st.wkpos[par] = c * 16;
+    }
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
