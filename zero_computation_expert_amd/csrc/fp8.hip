@@ -147,15 +147,19 @@ static hipError_t launch_quant(const void *src, int dtype, int64_t nmat, int row
   return hipGetLastError();
 }
 
-// x's exponent rows in permuted order: sxp[row] = sx[tok[row]] for the
-// P = meta[1] permuted rows (one thread per byte; pmax bounds the grid).
+// x's exponents in permuted row order, K-block-major: sxp[kb * ldt + row] =
+// sx[tok[row] * nkb + kb] for the P = meta[1] permuted rows (one thread per
+// byte, consecutive threads on consecutive rows; ldt * nkb bounds the grid),
+// so the expert GEMMs read one step's exponents of a tile's rows as
+// consecutive bytes.
 __global__ void gather_exp_kernel(const uint8_t *__restrict__ sx, const int32_t *__restrict__ tok,
-                                  const int32_t *__restrict__ meta, int nkb,
+                                  const int32_t *__restrict__ meta, int nkb, int64_t ldt,
                                   uint8_t *__restrict__ sxp) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t row = i / nkb;
-  if (row >= meta[1]) return;
-  sxp[i] = sx[static_cast<int64_t>(tok[row]) * nkb + (i - row * nkb)];
+  const int64_t kb = i / ldt;
+  const int64_t row = i - kb * ldt;
+  if (kb >= nkb || row >= meta[1]) return;
+  sxp[i] = sx[static_cast<int64_t>(tok[row]) * nkb + kb];
 }
 
 // The forward's activation quantization: x [T, d] -> qx, sx, then sx's rows
@@ -167,7 +171,7 @@ hipError_t launch_quant_x(const Plan &p, hipStream_t s) {
   const int nkb = p.d / 128;
   const int64_t n = p.pmax * nkb;
   hipLaunchKernelGGL(gather_exp_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                     s, p.sx, p.tok, p.meta, nkb, p.sxp);
+                     s, p.sx, p.tok, p.meta, nkb, p.pmax, p.sxp);
   return hipGetLastError();
 }
 

@@ -91,30 +91,6 @@ __device__ __forceinline__ void load_frags(uint4 (&A)[2], uint4 (&B)[NBR], const
     B[nb] = *reinterpret_cast<const uint4 *>(tb + nb * 32 * kPitch + chunk);
 }
 
-// Token rows of one K-step, gathered straight into LDS: instruction i of
-// wave w fills tile rows (4i + w)*8 .. +7, lane (row lr, position p) loading
-// logical chunk p ^ lds_swz(row) of its row (the swizzle the fragment reads
-// expect; bit 3 of those rows is w's bit 0, so the chunk is fixed per lane).
-// Rows past the chunk's end and steps past K read zeros (kOOB offset); the
-// instruction is issued regardless, so every step issues exactly NBR token
-// loads.
-template <typename T, int NBR>
-__device__ __forceinline__ void load_t(char *tile, const uint32_t (&tvo)[NBR],
-                                       const TileState<NBR> &st, int ks, int wave) {
-  constexpr int KC = 128 / sizeof(T);
-  const bool ok = ks * KC + st.tkpos < st.K;
-#pragma unroll
-  for (int i = 0; i < NBR; ++i) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        st.rb, (lds_void *)(tile + ((i * 4 + wave) * 8) * kPitch), 16,
-        (ok && tvo[i] != kOOB) ? tvo[i] + ks * 128 : kOOB, 0, 0, 0);
-#else
-    (void)tile; (void)tvo; (void)st; (void)ok; (void)wave;
-#endif
-  }
-}
-
 // MFMAs of one K-step: per 16-byte piece q, 2 x NBR independent MFMAs
 // (consecutive MFMAs never share an accumulator) over the wave's two weight
 // fragments and the NBR live token fragments.  NBR is a compile-time count

@@ -44,8 +44,10 @@ struct GemmArgs {
   // FP8 experts: E8M0 exponents (2^(byte - 127)) of the 128-wide K blocks
   const uint8_t *sa;   // weights [N, nrows/128, K/128] (GATE_UP: W_gate)
   const uint8_t *sa2;  // GATE_UP: W_up, same layout
-  const uint8_t *sb;   // token rows [rows of src, K/128] (x or H)
-  uint8_t *out_s;      // GATE_UP: exponents of the quantized H [P, I/128]
+  const uint8_t *sb;   // token rows' exponents, K-block-major [K/128, ldt] (x's rows in
+                       // permuted order, or H's rows)
+  uint8_t *out_s;      // GATE_UP: exponents of the quantized H, [I/128, ldt]
+  int ldt;             // row length of those exponent matrices (>= the permuted rows)
 };
 
 template <typename T>
@@ -143,6 +145,30 @@ __device__ __forceinline__ void load_w(char *slot_wave, const TileState<NB> &st,
     (void)a;
     (void)o;
     (void)ok;
+#endif
+  }
+}
+
+// Token rows of one K-step, gathered straight into LDS: instruction i of
+// wave w fills tile rows (4i + w)*8 .. +7, lane (row lr, position p) loading
+// logical chunk p ^ lds_swz(row) of its row (the swizzle the fragment reads
+// expect; bit 3 of those rows is w's bit 0, so the chunk is fixed per lane).
+// Rows past the chunk's end and steps past K read zeros (kOOB offset); the
+// instruction is issued regardless, so every step issues exactly NBR token
+// loads.
+template <typename T, int NBR>
+__device__ __forceinline__ void load_t(char *tile, const uint32_t (&tvo)[NBR],
+                                       const TileState<NBR> &st, int ks, int wave) {
+  constexpr int KC = 128 / sizeof(T);
+  const bool ok = ks * KC + st.tkpos < st.K;
+#pragma unroll
+  for (int i = 0; i < NBR; ++i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        st.rb, (lds_void *)(tile + ((i * 4 + wave) * 8) * kPitch), 16,
+        (ok && tvo[i] != kOOB) ? tvo[i] + ks * 128 : kOOB, 0, 0, 0);
+#else
+    (void)tile; (void)tvo; (void)st; (void)ok; (void)wave;
 #endif
   }
 }

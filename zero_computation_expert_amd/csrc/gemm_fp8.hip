@@ -14,13 +14,15 @@
 // per column of B and per 32-wide K half; every lane of a row or token passes
 // the same byte, which scales the whole step) and accumulate in fp32.
 //
-// Everything else is the bf16 design of gemm.hip (direct-to-LDS weight ring,
-// register-staged token tile, the same LDS swizzle, explicit waits, XCD-aware tile order,
-// per-count tile bodies): per step the bytes moved and read from LDS are the
-// same as bf16's, for twice the K.  A tile's exponents (its token rows' and
-// its weight blocks' rows, K/128 bytes each) are copied into LDS once, in
-// the prologue, token-major per K block so that the per-step byte reads of
-// a wave's 32 tokens hit consecutive bytes.
+// Everything else is the bf16 design of gemm.hip (direct-to-LDS weight ring
+// and token-tile ring, the same LDS swizzle, explicit waits, XCD-aware tile
+// order, per-count tile bodies): per step the bytes moved and read from LDS
+// are the same as bf16's, for twice the K.  The weight blocks' exponents (two
+// rows of K/128 bytes) are copied into LDS once per tile.  The token rows'
+// exponents are stored K-block-major ([K/128, rows]), so the exponents of one
+// step's tile rows are contiguous: each lane loads its column tokens' bytes
+// for step ks + 2 with the step's other loads (one byte load per token
+// block), into a three-deep register ring.
 #include "gemm_common.h"
 
 namespace moezc {
@@ -67,23 +69,16 @@ __device__ __forceinline__ void load_frags8(Frag8 (&A)[2], Frag8 (&B)[NBR], cons
   }
 }
 
-// The MFMAs of one step.  The explicit wait covers the weight slot (filled
-// by direct-to-LDS loads, which the compiler tracks only in part): two
-// groups of NBR + 8 loads are younger than the weights of step ks.  The
-// step's exponents come from the tile's LDS copy: the weight blocks' (one
-// byte per 32-row block, the same for every lane) and this lane's column
-// tokens'.
+// The MFMAs of one step (its weights, tokens and token exponents landed at
+// the end of the previous step).  The weight blocks' exponents come from the
+// tile's LDS copy (one byte per 32-row block, the same for every lane), the
+// column tokens' from registers.
 template <int NBR>
 __device__ __forceinline__ void compute8(floatx16 (&acc)[2][NBR], const char *slot_wave,
                                          const char *tile, const uint8_t *sa_row0,
-                                         const uint8_t *sa_row1, const uint8_t *sb_col, int nkb,
-                                         int ks, int r, int h) {
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (NBR + 8)));
-  asm volatile("" ::: "memory");
+                                         const uint8_t *sa_row1, const int (&sb)[NBR], int ks,
+                                         int r, int h) {
   const int sa[2] = {sa_row0[ks], sa_row1[ks]};
-  int sb[NBR];
-#pragma unroll
-  for (int nb = 0; nb < NBR; ++nb) sb[nb] = sb_col[nb * 32 * nkb + ks];
   const char *tb = tile + r * kPitch;
   Frag8 A[2][2], B[2][NBR];
   load_frags8<NBR>(A[0], B[0], slot_wave, tb, r, h, 0);
@@ -99,19 +94,41 @@ __device__ __forceinline__ void compute8(floatx16 (&acc)[2][NBR], const char *sl
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int NB, int NBR, int S>
-__device__ __forceinline__ void kstep8(int ks, floatx16 (&acc)[2][NBR], char *w0, char *w1,
-                                       char *w2, uint4 (&xr)[2][NBR], const TileState<NBR> &st,
-                                       TileBuf<NB> *tile, const uint8_t *sa0, const uint8_t *sa1,
-                                       const uint8_t *sbc, int nkb, int r, int h, int brow,
-                                       int bp) {
-  char *const slot_now = S % 3 == 0 ? w0 : (S % 3 == 1 ? w1 : w2);
-  char *const slot_next = (S + 2) % 3 == 0 ? w0 : ((S + 2) % 3 == 1 ? w1 : w2);
-  load_b<fp8_t, NBR>(xr[S & 1], st, ks + 2);
-  load_w<fp8_t, NBR, kStreamOnce>(slot_next, st, ks + 2);
-  compute8<NBR>(acc, slot_now, tile[ks & 1], sa0, sa1, sbc, nkb, ks, r, h);
-  store_b<NBR>(tile[(ks + 1) & 1], xr[(S + 1) & 1], brow, bp);
-  tile_barrier();
+// Exponent bytes of K block ks of this lane's column tokens, one per live
+// token block: eo[nb] is the token's row offset in the K-block-major
+// exponent matrix (kOOB past the chunk); blocks past K read zeros.
+template <int NBR>
+__device__ __forceinline__ void load_e(int (&eb)[NBR], const __amdgpu_buffer_rsrc_t &re,
+                                       const uint32_t (&eo)[NBR], uint32_t ldt, int ks, int nks) {
+#pragma unroll
+  for (int nb = 0; nb < NBR; ++nb)
+    eb[nb] = __builtin_amdgcn_raw_buffer_load_b8(
+        re, static_cast<int>((ks < nks && eo[nb] != kOOB) ? eo[nb] + static_cast<uint32_t>(ks) * ldt
+                                                          : kOOB),
+        0, 0);
+}
+
+// One K-step (S = ks mod 3 picks the ring slots at compile time): the token
+// exponents, token rows and weights of step ks + 2, the MFMAs of step ks,
+// then the wait that leaves only step ks + 2's 2 NBR + 8 loads in flight and
+// the barrier that publishes step ks + 1.
+template <int NBR, int S>
+__device__ __forceinline__ void kstep8(int ks, int nks, floatx16 (&acc)[2][NBR],
+                                       char *const (&w)[3], char *const (&tl)[3],
+                                       int (&eb)[3][NBR], const TileState<NBR> &st,
+                                       const uint32_t (&tvo)[NBR],
+                                       const __amdgpu_buffer_rsrc_t &re, const uint32_t (&eo)[NBR],
+                                       uint32_t ldt, const uint8_t *sa0, const uint8_t *sa1, int r,
+                                       int h, int wave) {
+  load_e<NBR>(eb[(S + 2) % 3], re, eo, ldt, ks + 2, nks);
+  load_t<fp8_t, NBR>(tl[(S + 2) % 3], tvo, st, ks + 2, wave);
+  load_w<fp8_t, NBR, kStreamOnce>(w[(S + 2) % 3], st, ks + 2);
+  asm volatile("" ::: "memory");
+  compute8<NBR>(acc, w[S], tl[S], sa0, sa1, eb[S], ks, r, h);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NBR + 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Smallest power of two >= amax / 448 as an exponent (clamped to E8M0's
@@ -147,8 +164,8 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
 
 template <int MODE, int NB, int NBR>
 __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, char *s_w0,
-                                           char *s_w1, char *s_w2, TileBuf<NB> *s_tile,
-                                           uint8_t *s_sa, uint8_t *s_sb) {
+                                           char *s_w1, char *s_w2, char *s_t0, char *s_t1,
+                                           char *s_t2, uint8_t *s_sa) {
   constexpr int KC = 128;  // FP8 elements per 128-byte step (= one scale block)
   const int e = t.e, rb = t.rb, m0 = t.m0, mcount = t.mcount;
   const int lane = threadIdx.x & 63;
@@ -173,46 +190,51 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
     st.ra[0] = st.ra[1] =
         make_rsrc(static_cast<const char *>(g.wa) + e * g.w_expert_stride, wbytes);
   }
-  {
-    const int lr = lane >> 3;
+  const int lr = lane >> 3;
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {  // 8-row groups with row bit 3 clear / set
-      const int c = (lane & 7) ^ lds_swz(par * 8 + lr);
-      st.wchunk[par] = c * 16;
-      st.wkpos[par] = c * 16;
-    }
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        st.wrow[a][j] = static_cast<uint32_t>(min(rowbase[a] + j * 8 + lr, g.nrows - 1)) * K;
+  for (int par = 0; par < 2; ++par) {  // 8-row groups with row bit 3 clear / set
+    const int c = (lane & 7) ^ lds_swz(par * 8 + lr);
+    st.wchunk[par] = c * 16;
+    st.wkpos[par] = c * 16;
   }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      st.wrow[a][j] = static_cast<uint32_t>(min(rowbase[a] + j * 8 + lr, g.nrows - 1)) * K;
 
-  // token rows (staged into LDS) and this lane's column tokens (exponents)
-  const int bp = threadIdx.x & 7;
-  const int brow = threadIdx.x >> 3;
-  st.kpos_b = bp * 16;
+  // token rows, direct to LDS: instruction i of wave w fills tile rows
+  // (4i + w)*8 .. +7 (bit 3 of those rows is w's bit 0)
+  const int tchunk = (lane & 7) ^ lds_swz((wave & 1) * 8 + lr);
+  st.tkpos = tchunk * 16;
   if (MODE == MODE8_GATE_UP) {
     st.rb = make_rsrc(g.src, static_cast<uint32_t>(g.T) * K);
   } else {
     st.rb = make_rsrc(static_cast<const char *>(g.src) + static_cast<int64_t>(m0) * K,
                       static_cast<uint32_t>(mcount) * K);
   }
+  uint32_t tvo[NBR];
 #pragma unroll
   for (int i = 0; i < NBR; ++i) {
-    const int tr = brow + 32 * i;
+    const int tr = (i * 4 + wave) * 8 + lr;
     // clamped index load whose value is always used (kOOB added for rows
     // past the chunk), so the NBR loads issue together
     const uint32_t row = MODE == MODE8_GATE_UP ? static_cast<uint32_t>(g.tok[m0 + min(tr, mcount - 1)])
                                                : static_cast<uint32_t>(tr);
-    st.vob[i] = row * K + bp * 16 + (tr < mcount ? 0u : kOOB);
+    tvo[i] = row * K + tchunk * 16 + (tr < mcount ? 0u : kOOB);
   }
+  // this lane's column tokens' exponents: row m0 + nb*32 + r of each K block
+  const uint32_t ldt = static_cast<uint32_t>(g.ldt);
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(g.sb, static_cast<uint32_t>(nkb) * ldt);
+  uint32_t eo[NBR];
+#pragma unroll
+  for (int nb = 0; nb < NBR; ++nb)
+    eo[nb] = nb * 32 + r < mcount ? static_cast<uint32_t>(m0 + nb * 32 + r) : kOOB;
 
-  // Exponents into LDS, once per tile.  s_sa: two rows of nkb bytes, the
-  // weight blocks this workgroup reads (GATE_UP: W_gate's and W_up's block
-  // rb; DOWN: W_down's blocks 2 rb and 2 rb + 1, waves 0-1 and 2-3).  s_sb:
-  // [mcount][nkb], the exponent rows of the tile's token rows (x's rows
-  // gathered into permuted order, or H's rows), then 127 for padding.
+  // The weight blocks' exponents into LDS, once per tile: two rows of nkb
+  // bytes (GATE_UP: W_gate's and W_up's block rb; DOWN: W_down's blocks 2 rb
+  // and 2 rb + 1, waves 0-1 and 2-3).  Done before the first tile loads, so
+  // the waits these loads need do not hold up the load pipeline.
   for (int i = threadIdx.x; i < 2 * nkb; i += kThreads) {
     const int which = i / nkb, kb = i - which * nkb;
     const uint8_t *src_e = MODE == MODE8_GATE_UP
@@ -223,43 +245,15 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
     const bool ok = MODE == MODE8_GATE_UP || (2 * rb + which) * 128 < g.nrows;
     s_sa[i] = ok ? src_e[kb] : 0;
   }
-  {
-    // the tile's token exponent rows are contiguous (permuted row order):
-    // copy mcount * nkb bytes, all loads issued before the stores
-    const uint8_t *src_e = g.sb + static_cast<int64_t>(m0) * nkb;
-    const int nbytes = mcount * nkb;
-    constexpr int kMaxDw = (kMaxKb8 * NB * 32 / 4 + kThreads - 1) / kThreads;
-    if (((reinterpret_cast<uintptr_t>(src_e) | static_cast<uintptr_t>(nbytes)) & 3) == 0) {
-      const uint32_t *s32 = reinterpret_cast<const uint32_t *>(src_e);
-      uint32_t *d32 = reinterpret_cast<uint32_t *>(s_sb);
-      const int nd = nbytes / 4;
-      uint32_t v[kMaxDw];
-#pragma unroll
-      for (int u = 0; u < kMaxDw; ++u) {
-        const int i = threadIdx.x + u * kThreads;
-        v[u] = i < nd ? s32[i] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < kMaxDw; ++u) {
-        const int i = threadIdx.x + u * kThreads;
-        if (i < nd) d32[i] = v[u];
-      }
-    } else {
-      for (int i = threadIdx.x; i < nbytes; i += kThreads) s_sb[i] = src_e[i];
-    }
-    // padding columns: exponent 127 (a scale of 1) on their zero data
-    for (int i = nbytes + threadIdx.x; i < NBR * 32 * nkb; i += kThreads) s_sb[i] = 127;
-  }
   const uint8_t *sa0 = MODE == MODE8_GATE_UP ? s_sa : s_sa + (wave >> 1) * nkb;
   const uint8_t *sa1 = MODE == MODE8_GATE_UP ? s_sa + nkb : sa0;
-  const uint8_t *sbc = s_sb + r * nkb;  // this lane's column token in token block 0
 
   const int nks = (K + KC - 1) / KC;
-  char *const w0 = s_w0 + wave * kWaveRowBytes;
-  char *const w1 = s_w1 + wave * kWaveRowBytes;
-  char *const w2 = s_w2 + wave * kWaveRowBytes;
+  char *const w[3] = {s_w0 + wave * kWaveRowBytes, s_w1 + wave * kWaveRowBytes,
+                      s_w2 + wave * kWaveRowBytes};
+  char *const tl[3] = {s_t0, s_t1, s_t2};
 
-  uint4 xr[2][NBR];
+  int eb[3][NBR];
   floatx16 acc[2][NBR];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -268,29 +262,28 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][nb][i] = 0.0f;
 
-  // prologue: the loads of steps 0 and 1 in the main loop's group order
-  load_b<fp8_t, NBR>(xr[0], st, 0);
-  load_w<fp8_t, NBR, kStreamOnce>(w0, st, 0);
+  // prologue: steps 0 and 1 in the loop's per-step load order
+  load_e<NBR>(eb[0], re, eo, ldt, 0, nks);
+  load_t<fp8_t, NBR>(tl[0], tvo, st, 0, wave);
+  load_w<fp8_t, NBR, kStreamOnce>(w[0], st, 0);
   asm volatile("" ::: "memory");
-  store_b<NBR>(s_tile[0], xr[0], brow, bp);
-  load_b<fp8_t, NBR>(xr[1], st, 1);
-  load_w<fp8_t, NBR, kStreamOnce>(w1, st, 1);
-  tile_barrier();  // also publishes the exponent copies
+  load_e<NBR>(eb[1], re, eo, ldt, 1, nks);
+  load_t<fp8_t, NBR>(tl[1], tvo, st, 1, wave);
+  load_w<fp8_t, NBR, kStreamOnce>(w[1], st, 1);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NBR + 8));
+  asm volatile("" ::: "memory");
+  tile_barrier();  // also publishes the weight exponents
 
   int ks = 0;
-  for (; ks + 6 <= nks; ks += 6) {
-    kstep8<NB, NBR, 0>(ks, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
-    kstep8<NB, NBR, 1>(ks + 1, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
-    kstep8<NB, NBR, 2>(ks + 2, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
-    kstep8<NB, NBR, 3>(ks + 3, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
-    kstep8<NB, NBR, 4>(ks + 4, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
-    kstep8<NB, NBR, 5>(ks + 5, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
+  for (; ks + 3 <= nks; ks += 3) {
+    kstep8<NBR, 0>(ks, nks, acc, w, tl, eb, st, tvo, re, eo, ldt, sa0, sa1, r, h, wave);
+    kstep8<NBR, 1>(ks + 1, nks, acc, w, tl, eb, st, tvo, re, eo, ldt, sa0, sa1, r, h, wave);
+    kstep8<NBR, 2>(ks + 2, nks, acc, w, tl, eb, st, tvo, re, eo, ldt, sa0, sa1, r, h, wave);
   }
-  if (ks < nks) kstep8<NB, NBR, 0>(ks, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
-  if (ks + 1 < nks) kstep8<NB, NBR, 1>(ks + 1, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
-  if (ks + 2 < nks) kstep8<NB, NBR, 2>(ks + 2, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
-  if (ks + 3 < nks) kstep8<NB, NBR, 3>(ks + 3, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
-  if (ks + 4 < nks) kstep8<NB, NBR, 4>(ks + 4, acc, w0, w1, w2, xr, st, s_tile, sa0, sa1, sbc, nkb, r, h, brow, bp);
+  if (ks < nks) kstep8<NBR, 0>(ks, nks, acc, w, tl, eb, st, tvo, re, eo, ldt, sa0, sa1, r, h, wave);
+  if (ks + 1 < nks)
+    kstep8<NBR, 1>(ks + 1, nks, acc, w, tl, eb, st, tvo, re, eo, ldt, sa0, sa1, r, h, wave);
 
   // drain the prefetches past the end of K before LDS is reused or released
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -300,9 +293,9 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
   // gi*8 + h*4 + [0, 4) in acc elements gi*4 .. gi*4+3.
   if (MODE == MODE8_DOWN) {
     // bf16 Y staged through wave-private LDS rows, as in the bf16 kernel; the
-    // barrier covers every wave's last loads and token-tile writes
+    // barrier follows every wave's drain of its own direct-to-LDS loads
     tile_barrier();
-    char *const stg = wave == 0 ? s_tile[0] : (wave == 1 ? s_tile[1] : (wave == 2 ? s_w0 : s_w1));
+    char *const stg = wave == 0 ? s_t0 : (wave == 1 ? s_t1 : (wave == 2 ? s_t2 : s_w0));
     stage_epilogue<MODE_DOWN, NBR>(g.out, nullptr, g.out_ld, g.nrows, t, acc, stg, rowbase[0], r,
                                    h, lane);
     return;
@@ -324,11 +317,10 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
     if (h == 0) s_amax_mine[nb * 32 + r] = m;
   }
   tile_barrier();
-  const int nkb_i = g.nrows / 128;  // H exponent row length (I / 128)
   // The workgroup's 128 quantized features of a token row are one 128-byte
   // line: the four waves write their 32 bytes of every row into one shared
   // LDS tile (16-byte chunks XOR-swizzled by row), then store whole lines.
-  char *const hs = s_tile[0];
+  char *const hs = s_t0;
 #pragma unroll
   for (int nb = 0; nb < NBR; ++nb) {
     const int col = nb * 32 + r;
@@ -350,8 +342,8 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
                      silu_mul(ga[gi * 4 + 2], ua[gi * 4 + 2]) * inv,
                      silu_mul(ga[gi * 4 + 3], ua[gi * 4 + 3]) * inv);
     }
-    if (wave == 0 && h == 0 && col < mcount)
-      g.out_s[(static_cast<int64_t>(m0) + col) * nkb_i + rb] = static_cast<uint8_t>(ex + 127);
+    if (wave == 0 && h == 0 && col < mcount)  // K-block-major: [I/128, ldt]
+      g.out_s[static_cast<int64_t>(rb) * g.ldt + m0 + col] = static_cast<uint8_t>(ex + 127);
   }
   tile_barrier();
   // rows (4i + wave)*8 + lane/8, 16-byte chunk lane%8; rows past the chunk
@@ -374,16 +366,16 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs &g, const TileLoc &t, 
 
 template <int MODE, int NB>
 __device__ __forceinline__ void dispatch_tile8(const GemmArgs &g, const TileLoc &t, int nb_rt,
-                                               char *s_w0, char *s_w1, char *s_w2,
-                                               TileBuf<NB> *s_tile, uint8_t *s_sa, uint8_t *s_sb) {
+                                               char *s_w0, char *s_w1, char *s_w2, char *s_t0,
+                                               char *s_t1, char *s_t2, uint8_t *s_sa) {
   if constexpr (NB == 1) {
     (void)nb_rt;
-    gemm8_tile<MODE, NB, 1>(g, t, s_w0, s_w1, s_w2, s_tile, s_sa, s_sb);
+    gemm8_tile<MODE, NB, 1>(g, t, s_w0, s_w1, s_w2, s_t0, s_t1, s_t2, s_sa);
   } else {
     switch (nb_rt) {
-#define MOEZC_TILE8_CASE(n)                                                    \
-  case n:                                                              \
-    if constexpr (n <= NB) gemm8_tile<MODE, NB, n>(g, t, s_w0, s_w1, s_w2, s_tile, s_sa, s_sb); \
+#define MOEZC_TILE8_CASE(n)                                                                \
+  case n:                                                                                  \
+    if constexpr (n <= NB) gemm8_tile<MODE, NB, n>(g, t, s_w0, s_w1, s_w2, s_t0, s_t1, s_t2, s_sa); \
     break;
       MOEZC_TILE8_CASE(1)
       MOEZC_TILE8_CASE(2)
@@ -400,16 +392,20 @@ __device__ __forceinline__ void dispatch_tile8(const GemmArgs &g, const TileLoc 
 template <int MODE, int NB>
 __global__ void __launch_bounds__(kThreads) gemm8_kernel(GemmArgs g) {
   constexpr int MT = NB * 32;
+  // three weight slots and three token tiles as distinct LDS objects (the
+  // compiler tracks each one's direct-to-LDS loads separately): 156 KB at
+  // NB = 5, plus the weight blocks' exponents
   __shared__ __attribute__((aligned(16))) char s_w0[kWSlotBytes];
   __shared__ __attribute__((aligned(16))) char s_w1[kWSlotBytes];
   __shared__ __attribute__((aligned(16))) char s_w2[kWSlotBytes];
-  __shared__ __attribute__((aligned(16))) TileBuf<NB> s_tile[2];
+  __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t0;
+  __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t1;
+  __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t2;
   __shared__ __attribute__((aligned(16))) uint8_t s_sa[2 * kMaxKb8];
-  __shared__ __attribute__((aligned(16))) uint8_t s_sb[kMaxKb8 * NB * 32];
   const int v = xcd_tile(g.meta[0] * g.nrb);
   if (v < 0) return;
   const TileLoc t = locate_expert_tile(g, v, MT);
-  dispatch_tile8<MODE, NB>(g, t, (t.mcount + 31) / 32, s_w0, s_w1, s_w2, s_tile, s_sa, s_sb);
+  dispatch_tile8<MODE, NB>(g, t, (t.mcount + 31) / 32, s_w0, s_w1, s_w2, s_t0, s_t1, s_t2, s_sa);
 }
 
 template <int MODE>
@@ -438,6 +434,7 @@ hipError_t launch_gate_up8(const Plan &p, hipStream_t s) {
   g.sa2 = p.s_up;
   g.src = p.qx;
   g.sb = p.sxp;
+  g.ldt = static_cast<int>(p.pmax);
   g.tok = p.tok;
   g.offs = p.offs;
   g.chunk_off = p.chunk_off;
@@ -461,6 +458,7 @@ hipError_t launch_down8(const Plan &p, hipStream_t s) {
   g.sa = p.s_down;
   g.src = p.h;
   g.sb = p.sh;
+  g.ldt = static_cast<int>(p.pmax);
   g.offs = p.offs;
   g.chunk_off = p.chunk_off;
   g.meta = p.meta;

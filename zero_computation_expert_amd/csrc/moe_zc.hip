@@ -143,6 +143,13 @@ static bool fp8_dims_ok(const moe_zc_dims *dm, int *status) {
     *status = MOE_ZC_EINVAL;
     return false;
   }
+  // the K-block-major exponent matrices of the permuted rows are addressed
+  // through 32-bit offsets
+  const int64_t pmax = dm->T * std::min(dm->k, dm->N);
+  if (pmax * (std::max(dm->d, dm->N > 0 ? dm->I : 0) / 128) >= (int64_t(1) << 31)) {
+    *status = MOE_ZC_EINVAL;
+    return false;
+  }
   return true;
 }
 

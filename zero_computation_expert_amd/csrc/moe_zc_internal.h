@@ -197,8 +197,9 @@ struct Plan {
   void *y;              // [pmax, d] expert outputs
   void *qx;             // FP8 path: [T, d] E4M3 x
   uint8_t *sx;          // FP8 path: [T, d/128] exponents of x
-  uint8_t *sxp;         // FP8 path: [pmax, d/128] the same, rows in permuted order
-  uint8_t *sh;          // FP8 path: [pmax, I/128] exponents of H
+  uint8_t *sxp;         // FP8 path: [d/128, pmax] the same, rows in permuted order,
+                        // K-block-major (a step's exponents of a tile's rows are contiguous)
+  uint8_t *sh;          // FP8 path: [I/128, pmax] exponents of H, K-block-major
   // backward (moe_zc_backward); idx then holds the sanitized routing
   const void *dout;     // [T, d] output gradient
   void *dx;             // [T, d] input gradient
