@@ -410,7 +410,11 @@ def scmoe_bench(args, cfg, inp, dev):
           "two_chunks_two_streams": timed(lambda: layer(2, True))}
     print("[bench] scmoe " + " ".join(f"{k}={v:.3f}" for k, v in ms.items()), file=sys.stderr,
           flush=True)
-    best = min(("two_streams", "two_chunks_two_streams"), key=lambda k: ms[k])
+    # the headline is the fastest layer schedule; overlap_saving is what the
+    # best overlapped schedule gains (negative: loses) against the serial one
+    layers = ("serial", "two_streams", "two_chunks_serial", "two_chunks_two_streams")
+    best = min(layers, key=lambda k: ms[k])
+    best_overlap = min(("two_streams", "two_chunks_two_streams"), key=lambda k: ms[k])
     dense_flops = 6 * cfg.T * cfg.d * Id
     dense_tf = dense_flops / (ms["dense_only"] / 1e3) / 1e12
     res = {
@@ -423,7 +427,8 @@ def scmoe_bench(args, cfg, inp, dev):
                                f"Z={cfg.Z} k={cfg.k}) + dense SwiGLU FFN width {Id}, bf16",
                    "schedule": best},
         "schedules_ms": {k: round(v, 4) for k, v in ms.items()},
-        "overlap_saving": round(1.0 - ms[best] / ms["serial"], 4),
+        "overlap_schedule": best_overlap,
+        "overlap_saving": round(1.0 - ms[best_overlap] / ms["serial"], 4),
         "roofline": {"bound": "mfma", "kernel": "dense FFN on gemm8w_kernel (gate/up + down)",
                      "achieved": round(dense_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dense_tf / MFMA_BF16_PEAK_TFLOPS, 4),
