@@ -109,6 +109,18 @@ def test_routed_scale_all_zero_routing():
     assert np.abs(gate - 3.0 * np.take_along_axis(oprobs, idx.astype(np.int64), 1)).max() <= 3e-5
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_split_router_slices_summed_before_topk(dt):
+    """Few tokens, many experts, wide d: the router GEMM splits K into 16
+    slices and, with only 8 top-k blocks, the slices are summed by a separate
+    kernel before top-k.  T*E is odd here, so that kernel takes its
+    one-logit-per-thread form."""
+    cfg = synth.Config("split16_" + dt, T=127, d=2048, I=16, N=515, Z=256, k=12, dtype=dt,
+                       seed=17, bias_lo=-1e-3, bias_hi=1e-3)
+    assert (cfg.T * cfg.E) % 2 == 1
+    full_check(cfg, synth.host_inputs(cfg), poison=True)
+
+
 def test_maximum_expert_count_and_k():
     """The library's limits: E = 2048 experts (1024 FFN + 1024 zero), k = 64
     slots per token; the widest top-k variant and 8 router row blocks."""

@@ -114,8 +114,9 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 // that leaves the 256 CUs short of work
 // (decode-sized batches, few experts), the K range is split into `split`
 // slices of `kslice` elements (whole 128-byte steps, at least two per slice)
-// whose fp32 partial logits are summed by the top-k kernel in slice order
-// (at most kMaxSplit slices, so that sum stays short).
+// whose fp32 partial logits are summed in slice order (at most kMaxSplit
+// slices), by the top-k kernel or, for few tokens, by a slice-sum kernel
+// spread over the chip just before it.
 constexpr int kMaxSplit = 16;
 struct RouterSplit {
   int nb, split, kslice;

@@ -303,21 +303,66 @@ __global__ void zero_int_kernel(int32_t *p, int n) {
   if (i < n) p[i] = 0;
 }
 
+// Sum of a split router GEMM's K-slice partials, added in slice order (the
+// order the top-k kernel adds them in, so the logits are bit-identical),
+// written over slice 0.  V consecutive logits per thread.
+template <int V>
+__global__ void __launch_bounds__(256) slice_sum_kernel(float *__restrict__ logits, int split,
+                                                        int64_t part_stride, int64_t n) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * V;
+  if (i >= n) return;
+  float a[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) a[v] = logits[i + v];
+  for (int sl = 1; sl < split; ++sl) {
+    const float *src = logits + sl * part_stride + i;
+    float b[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) b[v] = src[v];
+#pragma unroll
+    for (int v = 0; v < V; ++v) a[v] += b[v];
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) logits[i + v] = a[v];
+}
+
+// With few tokens the top-k kernel runs on few blocks (one per 16 tokens),
+// and each of them would add up all K slices of its tokens: decode's 128
+// tokens read 16 slices x 768 logits each on 8 CUs.  Then the slices are
+// summed first by a kernel spread over the chip, and top-k reads one slice.
+static bool sum_slices_first(const Plan &p) {
+  const int64_t bytes = static_cast<int64_t>(p.rs.split) * p.T * p.E * 4;
+  return p.rs.split > 1 && p.nblk < 128 && bytes >= (int64_t(1) << 19);
+}
+
 hipError_t launch_topk(const Plan &p, hipStream_t s) {
+  int split = p.rs.split;
+  const int64_t n = p.T * p.E;
+  if (sum_slices_first(p)) {
+    if (n % 4 == 0)
+      hipLaunchKernelGGL(slice_sum_kernel<4>, dim3(static_cast<unsigned>((n / 4 + 255) / 256)),
+                         dim3(256), 0, s, p.logits, split, n, n);
+    else
+      hipLaunchKernelGGL(slice_sum_kernel<1>, dim3(static_cast<unsigned>((n + 255) / 256)),
+                         dim3(256), 0, s, p.logits, split, n, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    split = 1;
+  }
   dim3 grid(p.nblk), block(kTokPerBlk * kWave);
   int vpl = (p.E + kWave - 1) / kWave;
   if (vpl <= 4)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k, p.idx,
-                       p.gate, p.blockhist, p.routed_scale);
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p.logits, split, n, p.bias, p.T, p.E,
+                       p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
   else if (vpl <= 12)  // up to 768 experts
-    hipLaunchKernelGGL(topk_kernel<12>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k,
-                       p.idx, p.gate, p.blockhist, p.routed_scale);
+    hipLaunchKernelGGL(topk_kernel<12>, grid, block, 0, s, p.logits, split, n, p.bias, p.T, p.E,
+                       p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
   else if (vpl <= 16)
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k,
-                       p.idx, p.gate, p.blockhist, p.routed_scale);
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p.logits, split, n, p.bias, p.T, p.E,
+                       p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
   else
-    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p.logits, p.rs.split, p.T * p.E, p.bias, p.T, p.E, p.k,
-                       p.idx, p.gate, p.blockhist, p.routed_scale);
+    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p.logits, split, n, p.bias, p.T, p.E,
+                       p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
   return hipGetLastError();
 }
 
