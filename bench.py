@@ -86,11 +86,12 @@ def gate_up_kernel_name(cfg, fp8=False):
     workload: 160-token chunks (the 8-wave kernel) when experts average at
     least 96 rows, else 128 or 32 (the 4-wave kernel); fp32 always runs the
     4-wave kernel."""
-    if fp8:
-        return "gemm8_kernel<GATE_UP> (FP8 gate/up GEMM + SwiGLU + [1,128] quantization of H)"
     pmax = cfg.T * min(cfg.k, cfg.N)
     avg = pmax // cfg.N if cfg.N > 0 else 0
     nb = 5 if avg >= 96 else (4 if avg >= 24 else 1)
+    if fp8:
+        name = "gemm8f_w8_kernel<GATE_UP>" if nb == 5 else f"gemm8_kernel<GATE_UP,{nb}>"
+        return name + " (FP8 gate/up GEMM + SwiGLU + [1,128] quantization of H)"
     if cfg.dtype == "bf16":
         name = "gemm8w_kernel<GATE_UP,5>" if nb == 5 else f"gemm_kernel<bf16,GATE_UP,{nb}>"
     else:
