@@ -362,7 +362,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
   } else {
     ntiles = g.meta[0] * g.nrb;
   }
-  const int v = MODE == MODE_ROUTER ? xcd_tile(ntiles) : xcd_tile_grouped(ntiles, g.nrb);
+  const int v = MODE == MODE_ROUTER ? xcd_tile(ntiles) : xcd_tile_grouped(ntiles, xcd_group(g.nrb));
   if (v < 0) return;
 
   TileLoc t;
@@ -621,7 +621,7 @@ __global__ void __launch_bounds__(kThreads8) gemm8w_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t1;
   __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t2;
   const int ntiles = g.meta[0] * g.nrb;
-  const int v = xcd_tile_grouped(ntiles, g.nrb);
+  const int v = xcd_tile_grouped(ntiles, xcd_group(g.nrb));
   if (v < 0) return;
   TileLoc t = locate_expert_tile(g, v, MT);
   const int nb_rt = (t.mcount + 31) / 32;
@@ -640,7 +640,7 @@ __global__ void __launch_bounds__(kThreads8) gemm8w_kernel(GemmArgs g) {
 template <typename T, int MODE>
 static hipError_t launch_gemm_t(const GemmArgs &g, int nb, int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  const int64_t grid = MODE == MODE_ROUTER ? ((max_tiles + 7) / 8) * 8 : grouped_grid(max_tiles, g.nrb);
+  const int64_t grid = MODE == MODE_ROUTER ? ((max_tiles + 7) / 8) * 8 : grouped_grid(max_tiles, xcd_group(g.nrb));
   const dim3 gd(static_cast<unsigned>(grid)), bd(kThreads);
   if constexpr (std::is_same<T, bf16_t>::value && MODE != MODE_ROUTER) {
     if (nb == 5)  // 160-token chunks: two waves per SIMD

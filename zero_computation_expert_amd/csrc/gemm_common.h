@@ -280,9 +280,10 @@ __device__ __forceinline__ int xcd_tile(int ntiles) {
 
 // Workgroup -> tile index for the expert GEMMs: the tiles go to the 8 XCDs
 // in groups of G consecutive ones, dealt round-robin (group j to XCD j % 8).
-// With G = the row blocks of a token chunk, one group is a chunk's tiles
-// (for experts of more than kChunkGroup chunks, G/8 row blocks of an 8-chunk
-// group), which share token rows and weights in that XCD's L2.  Dealing the
+// A group of G >= nrb consecutive tiles (xcd_group) holds whole token
+// chunks' row blocks (for experts of more than kChunkGroup chunks, G/8 row
+// blocks of an 8-chunk group), which share token rows and weights in that
+// XCD's L2.  Dealing the
 // groups out keeps the XCDs' loads even when tiles differ in cost: with
 // contiguous eighths of the tile list, the XCDs holding a skewed workload's
 // hot experts ran 20-25% longer than the others.  Each XCD starts x/8 of the
@@ -302,6 +303,13 @@ __device__ __forceinline__ int xcd_tile_grouped(int ntiles, int G) {
   const int v = (rot * 8 + x) * G + l % G;
   return v < ntiles ? v : -1;
 }
+
+// Group size of xcd_tile_grouped for a launch with nrb row blocks per chunk:
+// at least 32, one tile per CU of an XCD, so that a group holds several row
+// blocks of a hot expert's 8-chunk group (they share its token rows) or
+// several small experts' chunks.  Against G = nrb: small -2.7%, skewed
+// -0.9%, prod -0.2% per step; G = 2 nrb was worse on small and prod.
+__host__ __device__ __forceinline__ int xcd_group(int nrb) { return nrb > 32 ? nrb : 32; }
 
 // Launch grid for xcd_tile_grouped covering every tile index below max_tiles.
 inline int64_t grouped_grid(int64_t max_tiles, int G) {

@@ -403,7 +403,7 @@ __global__ void __launch_bounds__(kThreads) gemm8_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t1;
   __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t2;
   __shared__ __attribute__((aligned(16))) uint8_t s_sa[2 * kMaxKb8];
-  const int v = xcd_tile_grouped(g.meta[0] * g.nrb, g.nrb);
+  const int v = xcd_tile_grouped(g.meta[0] * g.nrb, xcd_group(g.nrb));
   if (v < 0) return;
   const TileLoc t = locate_expert_tile(g, v, MT);
   dispatch_tile8<MODE, NB>(g, t, (t.mcount + 31) / 32, s_w0, s_w1, s_w2, s_t0, s_t1, s_t2, s_sa);
@@ -734,7 +734,7 @@ __global__ void __launch_bounds__(kThreadsF8) gemm8f_w8_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t1;
   __shared__ __attribute__((aligned(16))) TileBuf<NB> s_t2;
   __shared__ __attribute__((aligned(16))) uint8_t s_sa[2 * kMaxKb8];
-  const int v = xcd_tile_grouped(g.meta[0] * g.nrb, g.nrb);
+  const int v = xcd_tile_grouped(g.meta[0] * g.nrb, xcd_group(g.nrb));
   if (v < 0) return;
   const TileLoc t = locate_expert_tile(g, v, MT);
   char *const s_w[3] = {s_w0, s_w1, s_w2};
@@ -752,7 +752,7 @@ __global__ void __launch_bounds__(kThreadsF8) gemm8f_w8_kernel(GemmArgs g) {
 template <int MODE>
 static hipError_t launch_gemm8(const GemmArgs &g, int nb, int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  const dim3 gd(static_cast<unsigned>(grouped_grid(max_tiles, g.nrb))), bd(kThreads);
+  const dim3 gd(static_cast<unsigned>(grouped_grid(max_tiles, xcd_group(g.nrb)))), bd(kThreads);
   if (nb == 5)  // 160-token chunks: two waves per SIMD
     hipLaunchKernelGGL((gemm8f_w8_kernel<MODE>), gd, dim3(kThreadsF8), 0, s, g);
   else if (nb == 4)
