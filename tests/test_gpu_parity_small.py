@@ -245,11 +245,13 @@ def test_z0_and_k_equals_E():
     assert (cnt == cfg.T).all()
 
 
-@pytest.mark.parametrize("T", [700, 1700])
+@pytest.mark.parametrize("T", [700, 1700, 2600])
 def test_single_hot_expert_spans_many_chunks(T):
-    """Bias +10 on FFN expert 3: every token picks it (M_e = T: 5 or 11
-    chunks of 160 rows; above 8 chunks the tiles go in groups of 8 chunks
-    per row block), the rest of the slots route normally."""
+    """Bias +10 on FFN expert 3: every token picks it, the rest of the slots
+    route normally.  M_e = T rows in hot-expert chunks of 256 rows: 3, 7 or
+    11 chunks (the last one 188, 164 or 40 rows, so up to three of its four
+    64-token quarters are empty); above 8 chunks the tiles go in groups of 8
+    chunks per row block."""
     cfg = synth.Config("hot", T=T, d=256, I=128, N=12, Z=4, k=3, dtype="bf16", seed=11)
     inp = synth.host_inputs(cfg)
     b = inp["bias"].copy()
@@ -258,19 +260,31 @@ def test_single_hot_expert_spans_many_chunks(T):
     assert cnt[3] == cfg.T and (idx[:, 0] == 3).all()
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_hot_experts_several_row_blocks_and_a_partial_chunk_group(dt):
-    """Two FFN experts take every token (bias +10): each has 1700 rows = 11
-    chunks of 160 (the last one 100 rows), i.e. one full group of 8 chunks
-    per row block and a last, shorter group of 3; d = 640 and I = 384 give 3
-    gate/up row blocks of 128 and 3 down row blocks of 256 (the last one
-    half empty), so the grouped tile order runs over several row blocks."""
-    cfg = synth.Config("hot2", T=1700, d=640, I=384, N=6, Z=3, k=3, dtype=dt, seed=14)
+@pytest.mark.parametrize("dt,T", [("bf16", 2600), ("f32", 1700)])
+def test_hot_experts_several_row_blocks_and_a_partial_chunk_group(dt, T):
+    """Two FFN experts take every token (bias +10): 11 chunks each (bf16:
+    hot-expert chunks of 256 rows, the last one 40; fp32: chunks of 160, the
+    last one 100), i.e. one full group of 8 chunks per row block and a last,
+    shorter group of 3; d = 640 and I = 384 give 3 gate/up row blocks of 128
+    and 3 down row blocks of 256 (the last one half empty), so the grouped
+    tile order runs over several row blocks."""
+    cfg = synth.Config("hot2", T=T, d=640, I=384, N=6, Z=3, k=3, dtype=dt, seed=14)
     inp = synth.host_inputs(cfg)
     b = inp["bias"].copy()
     b[[1, 4]] = 10.0
     _, cnt, idx, _ = full_check(cfg, inp, bias=b)
     assert cnt[1] == cnt[4] == cfg.T
+
+
+def test_hot_tiles_with_k_tails_and_partial_row_blocks():
+    """bf16, every FFN expert above 160 rows (hot-expert tiles of 256 rows):
+    d = 200 and I = 72 are not multiples of those tiles' 32-element K-step
+    (the last step reads zeros past K), I is below one 128-row gate/up block
+    and d below one 256-row down block (rows past them are clamped and
+    their outputs dropped)."""
+    cfg = synth.Config("hot_ktail", T=600, d=200, I=72, N=4, Z=2, k=3, dtype="bf16", seed=21)
+    _, cnt, _, _ = full_check(cfg, synth.host_inputs(cfg), poison=True)
+    assert (cnt[:cfg.N] > 160).sum() >= 2
 
 
 def test_empty_and_single_token():

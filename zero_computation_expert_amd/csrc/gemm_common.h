@@ -48,6 +48,8 @@ struct GemmArgs {
                        // permuted order, or H's rows)
   uint8_t *out_s;      // GATE_UP: exponents of the quantized H, [I/128, ldt]
   int ldt;             // row length of those exponent matrices (>= the permuted rows)
+  int hot_rows;        // bf16 GATE_UP / DOWN: experts with at least this many rows are
+                       // chunked kHotMT rows at a time (hot-expert tiles); 0: none
 };
 
 template <typename T>
@@ -219,6 +221,7 @@ using TileBuf = char[NB * 32 * kPitch];
 struct TileLoc {
   int e, rb, m0, mcount;
   int k0, klen, s;
+  int mt;  // chunk height of this tile's expert (kHotMT for a hot expert)
 };
 
 
@@ -236,7 +239,7 @@ struct TileLoc {
 constexpr int kChunkGroup = 8;
 __device__ __forceinline__ TileLoc locate_segment_tile(const int32_t *offs,
                                                        const int32_t *chunk_off, int N, int nrb,
-                                                       int v, int MT) {
+                                                       int v, int MT, int hot_rows = 0) {
   TileLoc t;
   t.k0 = 0;
   t.klen = 0;
@@ -257,13 +260,15 @@ __device__ __forceinline__ TileLoc locate_segment_tile(const int32_t *offs,
   const int within = local - grp * nrb * kChunkGroup;
   t.rb = within / gw;
   const int ch = grp * kChunkGroup + (within - t.rb * gw);
-  t.m0 = offs[t.e] + ch * MT;
-  t.mcount = min(MT, offs[t.e + 1] - t.m0);
+  const int rows = offs[t.e + 1] - offs[t.e];
+  t.mt = hot_rows > 0 && rows >= hot_rows ? kHotMT : MT;  // as the scan kernel chunked it
+  t.m0 = offs[t.e] + ch * t.mt;
+  t.mcount = min(t.mt, offs[t.e + 1] - t.m0);
   return t;
 }
 
 __device__ __forceinline__ TileLoc locate_expert_tile(const GemmArgs &g, int v, int MT) {
-  TileLoc t = locate_segment_tile(g.offs, g.chunk_off, g.N, g.nrb, v, MT);
+  TileLoc t = locate_segment_tile(g.offs, g.chunk_off, g.N, g.nrb, v, MT, g.hot_rows);
   t.klen = g.K;
   return t;
 }

@@ -205,6 +205,8 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   const int64_t avg_rows = dm->N > 0 ? p.pmax / dm->N : 0;
   p.nbmax = avg_rows >= 96 ? 5 : (avg_rows >= 24 ? 4 : 1);
   p.fp8 = f8 != nullptr;
+  // hot-expert tiles: bf16 experts on the 8-wave kernel (160-row chunks)
+  p.hot_rows = p.dtype == MOE_ZC_BF16 && !p.fp8 && p.nbmax == 5 ? kHotRows : 0;
   if (f8) {
     p.s_gate = f8->gate;
     p.s_up = f8->up;
@@ -507,6 +509,7 @@ static int dense_impl(int64_t T, int d, int Id, const void *x, const void *w1, c
   p.dtype = MOE_ZC_BF16;
   p.pmax = T;
   p.nbmax = T >= 96 ? 5 : (T >= 24 ? 4 : 1);
+  p.hot_rows = p.nbmax == 5 ? kHotRows : 0;
   p.x = x;
   p.w_gate = w1;
   p.w_up = w3;

@@ -231,7 +231,7 @@ __device__ int block_exclusive_scan(int v, int *s_tmp /* [16] */, int *total) {
 // Offsets of the FFN experts in permuted row order, and the prefix of GEMM
 // chunks (ceil(M_e / chunk_rows) per expert).  Single block.
 __global__ void __launch_bounds__(1024) expert_scan_kernel(const int32_t *__restrict__ counts,
-                                                           int N, int chunk_rows,
+                                                           int N, int chunk_rows, int hot_rows,
                                                            int32_t *__restrict__ offs,
                                                            int32_t *__restrict__ chunk_off,
                                                            int32_t *__restrict__ meta) {
@@ -240,7 +240,8 @@ __global__ void __launch_bounds__(1024) expert_scan_kernel(const int32_t *__rest
   for (int e0 = 0; e0 < N; e0 += 1024) {
     int e = e0 + threadIdx.x;
     int c = e < N ? counts[e] : 0;
-    int ch = (c + chunk_rows - 1) / chunk_rows;
+    const int rows = hot_rows > 0 && c >= hot_rows ? kHotMT : chunk_rows;
+    int ch = (c + rows - 1) / rows;
     int tot_r, tot_c;
     int ex_r = block_exclusive_scan(c, s_tmp, &tot_r);
     int ex_c = block_exclusive_scan(ch, s_tmp, &tot_c);
@@ -372,7 +373,7 @@ hipError_t launch_scan(const Plan &p, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.N == 0) return err;
   hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, s, p.counts, p.N, p.nbmax * 32,
-                     p.offs, p.chunk_off, p.meta);
+                     p.hot_rows, p.offs, p.chunk_off, p.meta);
   return hipGetLastError();
 }
 
@@ -383,14 +384,16 @@ hipError_t launch_permute(const Plan &p, hipStream_t s) {
 }
 
 // The dense FFN as one expert that every token uses: identity permutation,
-// one segment of T rows, ceil(T / chunk_rows) chunks.
-__global__ void dense_route_kernel(int64_t T, int chunk_rows, int32_t *__restrict__ tok,
-                                   int32_t *__restrict__ offs, int32_t *__restrict__ chunk_off,
-                                   int32_t *__restrict__ meta) {
+// one segment of T rows, ceil(T / rows) chunks (kHotMT rows from hot_rows
+// tokens up, as for a hot expert).
+__global__ void dense_route_kernel(int64_t T, int chunk_rows, int hot_rows,
+                                   int32_t *__restrict__ tok, int32_t *__restrict__ offs,
+                                   int32_t *__restrict__ chunk_off, int32_t *__restrict__ meta) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < T) tok[i] = static_cast<int32_t>(i);
   if (i == 0) {
-    const int nch = static_cast<int>((T + chunk_rows - 1) / chunk_rows);
+    const int rows = hot_rows > 0 && T >= hot_rows ? kHotMT : chunk_rows;
+    const int nch = static_cast<int>((T + rows - 1) / rows);
     offs[0] = 0;
     offs[1] = static_cast<int32_t>(T);
     chunk_off[0] = 0;
@@ -402,7 +405,7 @@ __global__ void dense_route_kernel(int64_t T, int chunk_rows, int32_t *__restric
 
 hipError_t launch_dense_route(const Plan &p, hipStream_t s) {
   hipLaunchKernelGGL(dense_route_kernel, dim3(static_cast<unsigned>((p.T + 255) / 256)), dim3(256),
-                     0, s, p.T, p.nbmax * 32, p.tok, p.offs, p.chunk_off, p.meta);
+                     0, s, p.T, p.nbmax * 32, p.hot_rows, p.tok, p.offs, p.chunk_off, p.meta);
   return hipGetLastError();
 }
 
