@@ -34,16 +34,21 @@
 //     zeros) and in consumption order, so the in-order vector-memory counter
 //     never makes a step wait for data of a later step.
 //   * Tiles are enumerated expert-major, row-block next, chunk fastest, and
-//     block ids are remapped so that consecutive tiles land on the same XCD
-//     (workgroups are dealt round-robin over the 8 XCDs): the row blocks of
-//     one expert share that expert's token rows in one L2, and the chunks of
-//     one row block share its weight rows.
+//     block ids are remapped so that groups of consecutive tiles land on the
+//     same XCD (xcd_tile_grouped; workgroups are dealt round-robin over the
+//     8 XCDs): the row blocks of one expert share that expert's token rows
+//     in one L2, and the chunks of one row block share its weight rows; the
+//     groups are dealt over the XCDs so that their loads stay even.
 //   * Expert weights and the outputs are touched once per launch and carry
 //     the non-temporal cache hint, so they do not evict those token rows;
 //     the router's weights, read by every token tile, do not.
 //   * bf16 outputs leave through the idle ring: each wave stages its output
 //     features of every token row in LDS and stores whole row segments
 //     (stage_epilogue), instead of 16-byte pieces scattered over 32 rows.
+//   * For 160-token chunks (bf16) the workgroup has 8 waves, two per SIMD
+//     (gemm8w_kernel), and experts of more than 160 rows run 256 x 256
+//     hot-expert tiles (gemm_hot_tile), which do more MFMA work per loaded
+//     and per LDS-read byte.
 #include "gemm_common.h"
 
 namespace moezc {
