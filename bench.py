@@ -141,14 +141,19 @@ def traffic_file(workload, kind):
 
 
 def kernel_source_hash(kind="gemm"):
-    """sha256 over the sources of the kernel whose traffic is reported
-    (gate/up GEMM: gemm.hip or gemm_fp8.hip; weight-gradient GEMM:
-    gemm_bwd.hip; each with gemm_common.h)."""
+    """sha256 over the code of the kernel whose traffic is reported (gate/up
+    GEMM: gemm.hip or gemm_fp8.hip; weight-gradient GEMM: gemm_bwd.hip; each
+    with gemm_common.h), with comments and whitespace removed, so that only a
+    change of code makes a measured traffic file stale."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        h.update(open(os.path.join(ROOT, "zero_computation_expert_amd", "csrc", f), "rb").read())
+        src = open(os.path.join(ROOT, "zero_computation_expert_amd", "csrc", f)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)  # block comments
+        src = re.sub(r"//[^\n]*", " ", src)  # line comments
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 
