@@ -5,11 +5,10 @@ oracle's.  The forward (moe_zc_forward_fp8) runs on weights that the oracle
 quantized on the host, so no oracle input comes from the HIP path; routing
 is checked as in the bf16 path (near-tie rule) and outputs against the
 oracle recomputed with the GPU's routing, with the bf16 path's tolerances.
-At full size the sampled tokens' experts are quantized on the host by the
-oracle, while the GPU forward uses the GPU quantizer's output (bit-identical,
-by the first test)."""
-import concurrent.futures as cf
-import os
+At full size (every token at decode; at prod a set of tokens that covers
+every 32-row block of every expert's rows) the compared tokens' experts are
+quantized on the host by the oracle, while the GPU forward uses the GPU
+quantizer's output (bit-identical, by the first test)."""
 import time
 
 import numpy as np
@@ -130,11 +129,18 @@ def test_fp8_all_zero_routing_reads_no_expert_weights():
     assert np.isfinite(got).all() and P.rel_frob(got, ref) <= 2e-2
 
 
-def test_fp8_prod_full_size_sampled():
+def test_fp8_prod_full_size_block_cover():
     """Production shapes (T=8192, d=6144, 512 SwiGLU experts of 2048, 256 zero
-    experts, top-12): device-generated bf16 weights quantized on the GPU; the
-    sampled tokens' experts quantized on the host by the oracle."""
+    experts, top-12) with FP8 experts: routing on every token, and the output
+    of a cover of every 32-row block of every expert's permuted rows (every
+    tile of both FP8 expert GEMMs, each expert's partial last chunk included)
+    against the FP8 oracle.  The GPU forward runs on the GPU quantizer's
+    weights (bit-identical to the oracle's, first test); the oracle quantizes
+    each routed expert's bf16 matrices itself, on the host, streaming a few
+    experts at a time."""
     cfg = synth.PROD
+    t0 = time.time()
+    log = lambda m: print(f"[fp8 prod] {m} ({time.time() - t0:.0f}s)", flush=True)  # noqa: E731
     dinp = synth.device_inputs(cfg, DEV)
     qg, eg = moe.quantize_fp8(dinp["W_gate"], 128)
     qu, eu = moe.quantize_fp8(dinp["W_up"], 128)
@@ -142,30 +148,30 @@ def test_fp8_prod_full_size_sampled():
     out, cnt, idx, gate = moe.forward_fp8(dinp["x"], dinp["W_router"], dinp["bias"], qg, eg, qu, eu,
                                           qd, ed, cfg.N, cfg.Z, cfg.k)
     torch.cuda.synchronize()
-    out, cnt, idx = P.to_np(out), P.to_np(cnt), P.to_np(idx)
+    del qg, qu, qd, eg, eu, ed
+    torch.cuda.empty_cache()
+    out, cnt, idx, gate = P.to_np(out), P.to_np(cnt), P.to_np(idx), P.to_np(gate)
     x, wr, bias = synth.host_x(cfg), synth.host_router(cfg), synth.host_bias(cfg)
+    assert (x == P.to_np(dinp["x"])).all()
     logits = oracle.router_logits(x, wr, "bf16")
     oidx, _, omargin, oprobs = oracle.route_from_logits(logits, bias, cfg.k)
+    info = P.check_routing(cfg, bias, idx, gate, cnt, oidx, oprobs, omargin)
     P.check_counts_against_oracle(cfg, idx, cnt, oidx, omargin)
-    rng = np.random.default_rng(0)
-    rows = sorted(set(rng.choice(cfg.T, 12, replace=False).tolist()) | {0, cfg.T - 1})
+    near = np.nonzero(omargin < P.MARGIN)[0][:8]
+    rows, nblocks = F.block_cover_rows(idx, cfg.N, extra=list(near) + [0, cfg.T - 1])
+    log(f"routing ok, near_ties={info['near_ties']}; {len(rows)} tokens cover {nblocks} blocks")
 
-    def one(t):
-        experts = {}
-        for e in idx[t]:
-            e = int(e)
-            if e < cfg.N:
-                mats = [P.to_np(dinp["W_" + w][e]) for w in ("gate", "up", "down")]
-                experts[e] = tuple(a for m in mats for a in oracle.quantize_fp8(m, "bf16", 128))
-        g = oprobs[t, idx[t]].astype(np.float32)
-        return oracle.token_output_fp8(x[t], "bf16", cfg.N, idx[t], g, experts)
+    def fetch(e):
+        mats = [P.to_np(dinp["W_" + w][e]) for w in ("gate", "up", "down")]
+        return tuple(a for m in mats for a in oracle.quantize_fp8(m, "bf16", 128))
 
-    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-        ref = np.stack(list(ex.map(one, rows)))
+    g = np.take_along_axis(oprobs, idx.astype(np.int64), 1).astype(np.float32)
+    ref = F.streamed_reference(x, "bf16", cfg.N, idx, g, rows, fetch, ffn=oracle.ffn_pairs_fp8,
+                               log=log)
+    assert np.isfinite(P.out_as_f32(out, "bf16")).all()
     err, worst = P.check_outputs(P.out_as_f32(out[rows], "bf16"), ref, "bf16")
-    print(f"[fp8] prod sampled {len(rows)} tokens rel_frob={err:.3e} worst_token={worst:.3e}",
-          flush=True)
-    del dinp, qg, qu, qd
+    log(f"{len(rows)} tokens rel_frob={err:.3e} worst_token={worst:.3e}")
+    del dinp
     torch.cuda.empty_cache()
 
 

@@ -108,18 +108,18 @@ def test_decode_full_size():
 
 def test_prod_full_size():
     cnt, idx, rows = run_full(synth.PROD, "cover")
-    # every expert with more than one chunk of 160 rows has its last,
-    # partial chunk covered (by construction of the cover; checked here)
+    # every expert above 160 rows (one hot-expert chunk of 256 rows each) has
+    # its rows past 160 covered (by construction of the cover; checked here)
     tt, _, ee, pos = F.permuted_positions(idx, synth.PROD.N)
     sel = np.isin(tt, rows)
     for e in np.nonzero(cnt[: synth.PROD.N] > 160)[0]:
-        assert (pos[sel & (ee == e)] >= (cnt[e] - 1) // 160 * 160).any()
+        assert (pos[sel & (ee == e)] >= 160).any()
 
 
 def test_skewed_full_size():
     cnt, idx, rows = run_full(synth.SKEWED, "cover")
     assert cnt[0] == synth.SKEWED.T  # the Zipf head expert takes every token
-    # its 103 chunks of 160 rows: every one (and every 32-row block) compared
+    # its 64 hot-expert chunks of 256 rows: every 32-row block compared
     tt, _, ee, pos = F.permuted_positions(idx, synth.SKEWED.N)
     hot = np.unique(pos[(ee == 0) & np.isin(tt, rows)] // 32)
     assert hot.size == (synth.SKEWED.T + 31) // 32
