@@ -404,15 +404,21 @@ void oracle_quantize_fp8(const void *src, int dt, int64_t nmat, int rows, int K,
   }
 }
 
+/* The value of every E4M3 byte (oracle_e4m3_to_f32 of each), so that the
+ * dot products below look values up instead of decoding each byte again. */
+static void orc_e4m3_table(float *lut) {
+  for (int q = 0; q < 256; ++q) lut[q] = oracle_e4m3_to_f32((uint8_t)q);
+}
+
 /* One row of a block-scaled GEMM: sum over K blocks of
- * (sa[kb] * sb[kb]) * (sum of the quantized products in the block). */
+ * (sa[kb] * sb[kb]) * (sum of the quantized products in the block).
+ * lut: orc_e4m3_table. */
 static float orc_dot_fp8(int K, const uint8_t *qa, const float *sa, const uint8_t *qb,
-                         const float *sb) {
+                         const float *sb, const float *lut) {
   float acc = 0.0f;
   for (int kb = 0; kb < K / 128; ++kb) {
     float blk = 0.0f;
-    for (int c = kb * 128; c < (kb + 1) * 128; ++c)
-      blk += oracle_e4m3_to_f32(qa[c]) * oracle_e4m3_to_f32(qb[c]);
+    for (int c = kb * 128; c < (kb + 1) * 128; ++c) blk += lut[qa[c]] * lut[qb[c]];
     const float sc = sa[kb] * sb[kb];
     acc += blk * sc;
   }
@@ -438,14 +444,18 @@ static void orc_expert_fp8(int d, int I, const uint8_t *qx, const float *sx, con
                            const uint8_t *qwd, const float *swd, float *h, uint8_t *qh,
                            float *sh, float *y) {
   const int dkb = d / 128, ikb = I / 128;
+  float lut[256];
+  orc_e4m3_table(lut);
   for (int r = 0; r < I; ++r) {
-    const float g = orc_dot_fp8(d, qwg + (int64_t)r * d, swg + (int64_t)(r / 128) * dkb, qx, sx);
-    const float u = orc_dot_fp8(d, qwu + (int64_t)r * d, swu + (int64_t)(r / 128) * dkb, qx, sx);
+    const float g =
+        orc_dot_fp8(d, qwg + (int64_t)r * d, swg + (int64_t)(r / 128) * dkb, qx, sx, lut);
+    const float u =
+        orc_dot_fp8(d, qwu + (int64_t)r * d, swu + (int64_t)(r / 128) * dkb, qx, sx, lut);
     h[r] = (g / (1.0f + expf(-g))) * u;
   }
   orc_quant_row(I, h, qh, sh);
   for (int i = 0; i < d; ++i)
-    y[i] = orc_dot_fp8(I, qwd + (int64_t)i * I, swd + (int64_t)(i / 128) * ikb, qh, sh);
+    y[i] = orc_dot_fp8(I, qwd + (int64_t)i * I, swd + (int64_t)(i / 128) * ikb, qh, sh, lut);
 }
 
 /* Steps 3-5 for one token with given routing, FP8 experts.  Pointer arrays
