@@ -5,8 +5,8 @@ oracle's.  The forward (moe_zc_forward_fp8) runs on weights that the oracle
 quantized on the host, so no oracle input comes from the HIP path; routing
 is checked as in the bf16 path (near-tie rule) and outputs against the
 oracle recomputed with the GPU's routing, with the bf16 path's tolerances.
-At full size (every token at decode; at prod a set of tokens that covers
-every 32-row block of every expert's rows) the compared tokens' experts are
+At full size (every token at decode; at prod and on the skewed workload a set
+of tokens that covers every 32-row block of every expert's rows) the compared tokens' experts are
 quantized on the host by the oracle, while the GPU forward uses the GPU
 quantizer's output (bit-identical, by the first test)."""
 import time
@@ -129,18 +129,16 @@ def test_fp8_all_zero_routing_reads_no_expert_weights():
     assert np.isfinite(got).all() and P.rel_frob(got, ref) <= 2e-2
 
 
-def test_fp8_prod_full_size_block_cover():
-    """Production shapes (T=8192, d=6144, 512 SwiGLU experts of 2048, 256 zero
-    experts, top-12) with FP8 experts: routing on every token, and the output
-    of a cover of every 32-row block of every expert's permuted rows (every
-    tile of both FP8 expert GEMMs, each expert's partial last chunk included)
+def run_fp8_full_cover(cfg, tag):
+    """Full-size FP8 forward: routing on every token, and the output of a
+    cover of every 32-row block of every expert's permuted rows (every tile
+    of both FP8 expert GEMMs, each expert's partial last chunk included)
     against the FP8 oracle.  The GPU forward runs on the GPU quantizer's
-    weights (bit-identical to the oracle's, first test); the oracle quantizes
-    each routed expert's bf16 matrices itself, on the host, streaming a few
-    experts at a time."""
-    cfg = synth.PROD
+    weights (bit-identical to the oracle's, first test); the oracle
+    quantizes each routed expert's bf16 matrices itself, on the host,
+    streaming a few experts at a time."""
     t0 = time.time()
-    log = lambda m: print(f"[fp8 prod] {m} ({time.time() - t0:.0f}s)", flush=True)  # noqa: E731
+    log = lambda m: print(f"[fp8 {tag}] {m} ({time.time() - t0:.0f}s)", flush=True)  # noqa: E731
     dinp = synth.device_inputs(cfg, DEV)
     qg, eg = moe.quantize_fp8(dinp["W_gate"], 128)
     qu, eu = moe.quantize_fp8(dinp["W_up"], 128)
@@ -159,7 +157,8 @@ def test_fp8_prod_full_size_block_cover():
     P.check_counts_against_oracle(cfg, idx, cnt, oidx, omargin)
     near = np.nonzero(omargin < P.MARGIN)[0][:8]
     rows, nblocks = F.block_cover_rows(idx, cfg.N, extra=list(near) + [0, cfg.T - 1])
-    log(f"routing ok, near_ties={info['near_ties']}; {len(rows)} tokens cover {nblocks} blocks")
+    log(f"routing ok, near_ties={info['near_ties']}; {len(rows)} tokens cover {nblocks} blocks, "
+        f"largest expert {int(cnt[: cfg.N].max())} rows")
 
     def fetch(e):
         mats = [P.to_np(dinp["W_" + w][e]) for w in ("gate", "up", "down")]
@@ -173,6 +172,19 @@ def test_fp8_prod_full_size_block_cover():
     log(f"{len(rows)} tokens rel_frob={err:.3e} worst_token={worst:.3e}")
     del dinp
     torch.cuda.empty_cache()
+
+
+def test_fp8_prod_full_size_block_cover():
+    """Production shapes (T=8192, d=6144, 512 SwiGLU experts of 2048, 256 zero
+    experts, top-12) with FP8 experts."""
+    run_fp8_full_cover(synth.PROD, "prod")
+
+
+def test_fp8_skewed_full_size_block_cover():
+    """The skewed workload (T=16384, one expert chosen by every token) with
+    FP8 experts: the hot expert's 103 chunks of 160 rows, in groups of 8 per
+    row block, every 32-row block compared."""
+    run_fp8_full_cover(synth.SKEWED, "skewed")
 
 
 def test_fp8_decode_full_size_every_token():
