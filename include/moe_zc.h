@@ -61,18 +61,21 @@ typedef enum {
   MOE_ZC_OK = 0,
   MOE_ZC_EINVAL = -1, /* a size, count or pointer argument is invalid        */
   MOE_ZC_EDTYPE = -2, /* dtype is neither MOE_ZC_F32 nor MOE_ZC_BF16          */
-  MOE_ZC_EALIGN = -3, /* a pointer is misaligned, or d / I not a multiple of 8 */
+  MOE_ZC_EALIGN = -3, /* a pointer is misaligned, or d / I not a multiple of 8
+                         (128 for FP8) where the entry point needs it        */
   MOE_ZC_ENOSPC = -4, /* workspace missing or smaller than the query          */
   MOE_ZC_EHIP = -5,   /* a HIP launch failed                                  */
   MOE_ZC_ESCRATCH = -6 /* moe_zc_forward_noalloc: the problem needs more than
                           MOE_ZC_SCRATCH_BYTES of workspace                   */
 } moe_zc_status;
 
-/* The problem.  Limits: T >= 0; d >= 8 and I >= 8, both multiples of 8;
- * N >= 0, Z >= 0, 1 <= N + Z <= 2048; 1 <= k <= min(64, N + Z);
- * T * k < 2^31; T * d and I * d (times the element size) below 2 GiB;
- * d and I at most 2^22; routed_scale finite and > 0.  I is ignored when
- * N == 0.
+/* The problem.  Limits: T >= 0; d >= 1 and I >= 1 (moe_zc_forward and
+ * moe_zc_forward_noalloc; the backward, FP8 and dense-FFN entry points need
+ * multiples of 8, and FP8 of 128); N >= 0, Z >= 0, 1 <= N + Z <= 2048;
+ * 1 <= k <= min(64, N + Z); T * k < 2^31; with d8 and I8 the widths rounded
+ * up to multiples of 8: T * d8 and I8 * d8 (times the element size) below
+ * 2 GiB, d8 and I8 at most 2^22; routed_scale finite and > 0.  I is ignored
+ * when N == 0.
  * routed_scale (LongCat-Flash-Lite article, part 02: the fused router kernel
  * ends with a scaling step; the pages do not say what it scales): every
  * selected slot's gate is routed_scale * p[idx] (FFN and zero slots alike),
@@ -91,7 +94,9 @@ typedef struct {
 } moe_zc_dims;
 
 /* Bytes of device workspace moe_zc_forward needs for `dims` (worst case:
- * every slot an FFN expert).  Returns 0 for invalid dims. */
+ * every slot an FFN expert; with d or I not a multiple of 8 also room for
+ * the zero-padded copies described at moe_zc_forward).  Returns 0 for
+ * invalid dims. */
 size_t moe_zc_workspace_bytes(const moe_zc_dims *dims);
 
 /* The forward pass, steps 1-5 above.
@@ -109,6 +114,15 @@ size_t moe_zc_workspace_bytes(const moe_zc_dims *dims);
  *                            the unbiased probabilities
  *   workspace  >= moe_zc_workspace_bytes(dims) bytes, 256-byte aligned;
  *              its contents on entry are ignored
+ * Widths that are not multiples of 8: the kernels move 16-byte row pieces,
+ * so the call first copies x, W_router, W_gate, W_up and W_down into the
+ * workspace with d and I rounded up to multiples of 8 and the new columns
+ * and rows zero, runs on those, and copies the first d columns of each
+ * output row back.  The result is the same as on the unpadded operands
+ * (every added product has an exact zero factor, and the added SwiGLU
+ * features, silu(0) * 0 = 0, meet zero columns of W_down).  The copies
+ * read all expert weights on every call: this path serves odd shapes, not
+ * speed; the stage timer does not include them.
  * Returns a moe_zc_status. */
 int moe_zc_forward(const moe_zc_dims *dims, const void *x, const void *W_router,
                    const float *bias, const void *W_gate, const void *W_up, const void *W_down,

@@ -67,17 +67,28 @@ EINVAL, EDTYPE, EALIGN, ENOSPC = -1, -2, -3, -4
     (D(N=100, Z=0, k=65), EINVAL),           # k > 64
     (D(d=0), EINVAL),
     (D(I=0), EINVAL),
-    (D(d=100), EALIGN),                      # not a multiple of 8
-    (D(I=60), EALIGN),
     (D(T=1 << 28, k=8), EINVAL),             # T * k >= 2^31
     (D(T=1 << 20, d=1024, k=2), EINVAL),     # x is 2 GiB of bf16
     (D(I=1 << 17, d=8192), EINVAL),          # one expert matrix is 2 GiB
     (D(T=8, d=(1 << 22) + 8, I=8), EINVAL),  # d above 2^22
     (D(T=8, d=8, I=(1 << 22) + 8), EINVAL),  # I above 2^22
+    (D(T=8, d=(1 << 22) + 1, I=8), EINVAL),  # d above 2^22, not a multiple of 8
 ])
 def test_invalid_dims(dims, expect):
     assert moe.lib().moe_zc_workspace_bytes(ctypes.byref(dims)) == 0
     assert call(dims, ws_bytes=1 << 40) == expect
+
+
+def test_widths_not_multiples_of_8_take_padded_workspace():
+    # the forward runs such widths on zero-padded copies inside its workspace
+    lib = moe.lib()
+    ws = lambda dims: lib.moe_zc_workspace_bytes(ctypes.byref(dims))  # noqa: E731
+    assert ws(D(d=100)) > ws(D(d=104)) > 0
+    assert ws(D(I=60)) > ws(D(I=64)) > 0
+    assert ws(D(d=1, I=1)) > 0 and ws(D(d=13, I=5, N=0, Z=4)) > 0
+    # still validated before anything is enqueued
+    assert call(D(d=100), ws_bytes=ws(D(d=104))) == ENOSPC
+    assert call(D(d=100), x=A + 8) == EALIGN
 
 
 def test_null_dims():
@@ -304,8 +315,9 @@ def test_scmoe_rejects():
 @pytest.mark.parametrize("dims,expect", [
     (D(dtype=7), EDTYPE),
     (D(k=0), EINVAL),
-    (D(d=100), EALIGN),
+    (D(d=0), EINVAL),
     (D(T=8192, d=6144, I=2048, N=512, Z=256, k=12), -6),  # needs ~1.5 GB > the static scratch
+    (D(T=4096, d=1000, I=1000, N=64, Z=32, k=6), -6),     # padded copies of every expert
 ])
 def test_noalloc_rejects_before_touching_the_device(dims, expect):
     """moe_zc_forward_noalloc validates like moe_zc_forward and rejects a

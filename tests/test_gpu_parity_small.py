@@ -82,6 +82,23 @@ def test_parity_full(cfg):
     full_check(cfg, synth.host_inputs(cfg), poison=True)
 
 
+# widths that are not multiples of 8: the forward's zero-padded path (one
+# element per row up to a whole 16-byte piece short), every element compared
+ODD = [
+    synth.Config("odd_bf16", T=77, d=100, I=36, N=6, Z=3, k=3, dtype="bf16", seed=16),
+    synth.Config("odd_f32", T=77, d=100, I=36, N=6, Z=3, k=3, dtype="f32", seed=16),
+    synth.Config("odd_narrow_bf16", T=33, d=13, I=5, N=4, Z=2, k=2, dtype="bf16", seed=17),
+    synth.Config("odd_one_bf16", T=20, d=1, I=1, N=3, Z=2, k=2, dtype="bf16", seed=19),
+    synth.Config("odd_d_only_bf16", T=300, d=1001, I=256, N=10, Z=5, k=4, dtype="bf16", seed=18),
+    synth.Config("odd_I_only_f32", T=170, d=256, I=250, N=12, Z=4, k=4, dtype="f32", seed=20),
+]
+
+
+@pytest.mark.parametrize("cfg", ODD, ids=lambda c: c.name)
+def test_widths_not_multiples_of_8(cfg):
+    full_check(cfg, synth.host_inputs(cfg), poison=True)
+
+
 @pytest.mark.parametrize("cfg,scale", [(RAGGED[1], 2.5), (RAGGED[2], 2.5), (RAGGED[5], 0.37)],
                          ids=["bf16-2.5", "f32-2.5", "wide-0.37"])
 def test_routed_scale(cfg, scale):

@@ -63,6 +63,20 @@ def test_noalloc_decode_shape_then_smaller():
     torch.cuda.empty_cache()
 
 
+def test_noalloc_widths_not_multiples_of_8():
+    """The zero-padded path (copies with d and I rounded up to 8, in the
+    shared array too), on two calls in a row, the second smaller."""
+    cfg = synth.Config("noalloc_odd", T=200, d=100, I=36, N=6, Z=3, k=3, dtype="bf16", seed=72)
+    h = synth.host_inputs(cfg)
+    inp = {n: (torch.from_numpy(v).view(torch.bfloat16) if v.dtype == np.uint16
+               else torch.from_numpy(v)).to(DEV) for n, v in h.items()}
+    for T in (200, 31):
+        print(f"[noalloc] d=100 I=36 T={T}", flush=True)
+        ref, got = _pair(inp, cfg.N, cfg.Z, cfg.k, T)
+        _same(ref, got)
+        assert int(got[1].sum()) == T * cfg.k
+
+
 def test_noalloc_rejects_a_problem_beyond_its_scratch():
     big = moe.make_dims(8192, 6144, 2048, 512, 256, 12, moe.BF16)
     assert moe.lib().moe_zc_workspace_bytes(ctypes.byref(big)) > moe.SCRATCH_BYTES

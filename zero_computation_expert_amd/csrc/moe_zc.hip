@@ -13,7 +13,12 @@ namespace moezc {
 
 static inline size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-static bool dims_ok(const moe_zc_dims *dm, int *status) {
+static inline int round8(int v) { return (v + 7) & ~7; }
+
+// pad_ok: the bf16 / fp32 forward, which takes any d, I >= 1 (widths that are
+// not multiples of 8 run on zero-padded copies, pad.hip); the other entry
+// points need multiples of 8.  Size limits apply to the padded widths.
+static bool dims_ok(const moe_zc_dims *dm, int *status, bool pad_ok = false) {
   if (dm == nullptr) {
     *status = MOE_ZC_EINVAL;
     return false;
@@ -24,7 +29,7 @@ static bool dims_ok(const moe_zc_dims *dm, int *status) {
   }
   const int64_t E = static_cast<int64_t>(dm->N) + dm->Z;
   if (dm->T < 0 || dm->N < 0 || dm->Z < 0 || E < 1 || E > kMaxE || dm->k < 1 || dm->k > E ||
-      dm->k > kMaxK || dm->d < 8 || (dm->N > 0 && dm->I < 8) ||
+      dm->k > kMaxK || dm->d < 1 || (dm->N > 0 && dm->I < 1) ||
       dm->T * static_cast<int64_t>(dm->k) >= (int64_t(1) << 31) ||
       !(dm->routed_scale > 0.0f && dm->routed_scale <= 3.4028234e38f)) {
     *status = MOE_ZC_EINVAL;
@@ -33,18 +38,22 @@ static bool dims_ok(const moe_zc_dims *dm, int *status) {
   // The expert GEMMs address x and one expert matrix through 32-bit buffer
   // offsets: both must stay below 2 GiB.
   const int64_t es = dm->dtype == MOE_ZC_BF16 ? 2 : 4;
-  if (dm->T * dm->d * es >= (int64_t(1) << 31) ||
-      (dm->N > 0 && static_cast<int64_t>(dm->I) * dm->d * es >= (int64_t(1) << 31))) {
+  if (dm->d > kMaxWidth || (dm->N > 0 && dm->I > kMaxWidth)) {
+    *status = MOE_ZC_EINVAL;
+    return false;
+  }
+  const int64_t d8 = round8(dm->d), I8 = dm->N > 0 ? round8(dm->I) : 0;
+  if (dm->T * d8 * es >= (int64_t(1) << 31) || I8 * d8 * es >= (int64_t(1) << 31)) {
     *status = MOE_ZC_EINVAL;
     return false;
   }
   // The expert GEMM epilogues store through tile-relative 32-bit offsets
   // (up to 160 rows of d or I elements).
-  if (dm->d > kMaxWidth || (dm->N > 0 && dm->I > kMaxWidth)) {
+  if (d8 > kMaxWidth || I8 > kMaxWidth) {
     *status = MOE_ZC_EINVAL;
     return false;
   }
-  if (dm->d % 8 != 0 || (dm->N > 0 && dm->I % 8 != 0)) {
+  if (!pad_ok && (dm->d % 8 != 0 || (dm->N > 0 && dm->I % 8 != 0))) {
     *status = MOE_ZC_EALIGN;
     return false;
   }
@@ -104,6 +113,54 @@ static size_t layout(const moe_zc_dims *dm, char *base, Plan *p, bool fp8 = fals
   return off;
 }
 
+// Widths that are not multiples of 8: the forward runs on the dims with d
+// and I rounded up (padded) and zero-padded copies of its operands.
+static bool needs_pad(const moe_zc_dims *dm) {
+  return dm->d % 8 != 0 || (dm->N > 0 && dm->I % 8 != 0);
+}
+
+static moe_zc_dims padded(const moe_zc_dims *dm) {
+  moe_zc_dims q = *dm;
+  q.d = round8(dm->d);
+  if (dm->N > 0) q.I = round8(dm->I);
+  return q;
+}
+
+struct PadBufs {
+  char *x, *wr, *wg, *wu, *wd, *out;  // padded x, W_router, W_gate, W_up, W_down, output
+};
+
+// Workspace of the padded copies (placed before the forward's own layout);
+// 0 when d and I are multiples of 8.  With base == nullptr only sizes.
+static size_t pad_layout(const moe_zc_dims *dm, char *base, PadBufs *b) {
+  if (!needs_pad(dm)) return 0;
+  const moe_zc_dims q = padded(dm);
+  const size_t es = dm->dtype == MOE_ZC_BF16 ? 2 : 4;
+  const size_t T = static_cast<size_t>(dm->T), E = static_cast<size_t>(dm->N + dm->Z);
+  const size_t N = static_cast<size_t>(dm->N), d8 = static_cast<size_t>(q.d);
+  const size_t I8 = dm->N > 0 ? static_cast<size_t>(q.I) : 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *ptr = base ? base + off : nullptr;
+    off = align_up(off + bytes);
+    return ptr;
+  };
+  char *x = take(T * d8 * es);
+  char *wr = take(E * d8 * es);
+  char *wg = take(N * I8 * d8 * es);
+  char *wu = take(N * I8 * d8 * es);
+  char *wd = take(N * d8 * I8 * es);
+  char *out = take(T * d8 * es);
+  if (b) *b = PadBufs{x, wr, wg, wu, wd, out};
+  return off;
+}
+
+// Workspace of the bf16 / fp32 forward.
+static size_t forward_bytes(const moe_zc_dims *dm) {
+  const moe_zc_dims q = padded(dm);
+  return pad_layout(dm, nullptr, nullptr) + layout(&q, nullptr, nullptr);
+}
+
 static bool aligned(const void *ptr, size_t a) {
   return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0;
 }
@@ -160,8 +217,12 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
                         moe_zc_timer *timer, const Fp8Scales *f8 = nullptr,
                         bool launch = true) {
   int st;
-  if (!(f8 ? fp8_dims_ok(dm, &st) : dims_ok(dm, &st))) return st;
+  if (!(f8 ? fp8_dims_ok(dm, &st) : dims_ok(dm, &st, true))) return st;
   if (f8 && dm->T > 0 && dm->N > 0 && (!f8->gate || !f8->up || !f8->down)) return MOE_ZC_EINVAL;
+  // widths that are not multiples of 8 (never FP8): the kernels run on q
+  const bool pad = needs_pad(dm);
+  const moe_zc_dims q = padded(dm);
+  const size_t padb = pad_layout(dm, nullptr, nullptr);
   const int64_t T = dm->T;
   const size_t es = dm->dtype == MOE_ZC_BF16 ? 2 : 4;
   const size_t xbytes = static_cast<size_t>(T) * dm->d * es;
@@ -177,7 +238,7 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
   const void *p4[] = {bias, counts, topk_idx, topk_gate};
   for (const void *ptr : p4)
     if (ptr && !aligned(ptr, 4)) return MOE_ZC_EALIGN;
-  const size_t need = layout(dm, nullptr, nullptr, f8 != nullptr);
+  const size_t need = padb + layout(&q, nullptr, nullptr, f8 != nullptr);
   if (T > 0) {
     if (workspace == nullptr || workspace_bytes < need) return MOE_ZC_ENOSPC;
     if (!aligned(workspace, 256)) return MOE_ZC_EALIGN;
@@ -187,8 +248,8 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
 
   Plan p = {};
   p.T = T;
-  p.d = dm->d;
-  p.I = dm->N > 0 ? dm->I : 0;
+  p.d = q.d;
+  p.I = dm->N > 0 ? q.I : 0;
   p.N = dm->N;
   p.Z = dm->Z;
   p.E = dm->N + dm->Z;
@@ -213,15 +274,17 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
     p.s_down = f8->down;
   }
   p.rs = router_split(T, p.d, p.E, p.dtype);
-  p.x = x;
-  p.w_router = w_router;
-  p.w_gate = w_gate;
-  p.w_up = w_up;
-  p.w_down = w_down;
+  PadBufs pb = {};
+  pad_layout(dm, static_cast<char *>(workspace), &pb);
+  p.x = pad ? pb.x : x;
+  p.w_router = pad ? pb.wr : w_router;
+  p.w_gate = pad ? pb.wg : w_gate;
+  p.w_up = pad ? pb.wu : w_up;
+  p.w_down = pad ? pb.wd : w_down;
   p.bias = bias;
-  p.out = out;
+  p.out = pad ? pb.out : out;
   p.counts = counts;
-  layout(dm, static_cast<char *>(workspace), &p, f8 != nullptr);
+  layout(&q, static_cast<char *>(workspace) + padb, &p, f8 != nullptr);
   if (topk_idx) p.idx = topk_idx;
   if (topk_gate) p.gate = topk_gate;
 
@@ -257,6 +320,18 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
       },
       launch_gate_up8, launch_down8, launch_combine};
   const Launch *run = p.fp8 ? stages8 : stages;
+  if (pad) {  // zero-padded operands (outside the timed stages)
+    const int es_i = static_cast<int>(es), E = dm->N + dm->Z;
+    if (launch_pad(x, 1, static_cast<int>(T), dm->d, pb.x, static_cast<int>(T), q.d, es_i, s) !=
+            hipSuccess ||
+        launch_pad(w_router, 1, E, dm->d, pb.wr, E, q.d, es_i, s) != hipSuccess)
+      return MOE_ZC_EHIP;
+    if (dm->N > 0 &&
+        (launch_pad(w_gate, dm->N, dm->I, dm->d, pb.wg, q.I, q.d, es_i, s) != hipSuccess ||
+         launch_pad(w_up, dm->N, dm->I, dm->d, pb.wu, q.I, q.d, es_i, s) != hipSuccess ||
+         launch_pad(w_down, dm->N, dm->d, dm->I, pb.wd, q.d, q.I, es_i, s) != hipSuccess))
+      return MOE_ZC_EHIP;
+  }
   if (!mark(0)) return MOE_ZC_EHIP;
   for (int i = 0; i < MOE_ZC_NSTAGES; ++i) {
     const bool ffn = i == MOE_ZC_STAGE_GATE_UP || i == MOE_ZC_STAGE_DOWN;
@@ -264,6 +339,8 @@ static int forward_impl(const moe_zc_dims *dm, const void *x, const void *w_rout
       if (run[i](p, s) != hipSuccess) return MOE_ZC_EHIP;
     if (!mark(i + 1)) return MOE_ZC_EHIP;
   }
+  if (pad && launch_unpad(pb.out, T, q.d, out, dm->d, static_cast<int>(es), s) != hipSuccess)
+    return MOE_ZC_EHIP;
   if (timer) timer->ncalls++;
   return MOE_ZC_OK;
 }
@@ -559,8 +636,8 @@ int moe_zc_forward_noalloc(const moe_zc_dims *dims, const void *x, const void *W
                            const void *W_down, void *out, int32_t *counts, int32_t *topk_idx,
                            float *topk_gate, void *stream) {
   int st;
-  if (!dims_ok(dims, &st)) return st;
-  const size_t need = layout(dims, nullptr, nullptr);
+  if (!dims_ok(dims, &st, true)) return st;
+  const size_t need = forward_bytes(dims);
   if (need > MOE_ZC_SCRATCH_BYTES) return MOE_ZC_ESCRATCH;
   // every other argument, before the device is touched (a stand-in address
   // with the scratch array's alignment takes the workspace's place)
@@ -595,8 +672,8 @@ int moe_zc_forward_fp8(const moe_zc_dims *dims, const void *x, const void *W_rou
 
 size_t moe_zc_workspace_bytes(const moe_zc_dims *dims) {
   int st;
-  if (!dims_ok(dims, &st)) return 0;
-  return layout(dims, nullptr, nullptr);
+  if (!dims_ok(dims, &st, true)) return 0;
+  return forward_bytes(dims);
 }
 
 int moe_zc_forward(const moe_zc_dims *dims, const void *x, const void *W_router,
@@ -710,7 +787,8 @@ const char *moe_zc_status_string(int status) {
     case MOE_ZC_OK: return "ok";
     case MOE_ZC_EINVAL: return "invalid argument (size, count or pointer)";
     case MOE_ZC_EDTYPE: return "unsupported dtype";
-    case MOE_ZC_EALIGN: return "misaligned pointer, or d / I not a multiple of 8";
+    case MOE_ZC_EALIGN:
+      return "misaligned pointer, or d / I not a multiple of 8 (FP8: 128) where required";
     case MOE_ZC_ENOSPC: return "workspace missing or too small (or timer full)";
     case MOE_ZC_EHIP: return "HIP launch failed";
     case MOE_ZC_ESCRATCH:

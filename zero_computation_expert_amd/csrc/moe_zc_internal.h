@@ -160,6 +160,13 @@ hipError_t launch_quant_x(const Plan &p, hipStream_t s);
 hipError_t launch_gate_up8(const Plan &p, hipStream_t s);
 hipError_t launch_down8(const Plan &p, hipStream_t s);
 hipError_t launch_dense_route(const Plan &p, hipStream_t s);  // dense FFN as one expert
+// zero-padded copies (pad.hip): dst [nmat, rows_p, cols_p] <- src [nmat, rows,
+// cols]; dst [rows, cols] <- the first cols columns of src [rows, cols_p];
+// es = element bytes (2 or 4)
+hipError_t launch_pad(const void *src, int64_t nmat, int rows, int cols, void *dst, int rows_p,
+                      int cols_p, int es, hipStream_t s);
+hipError_t launch_unpad(const void *src, int64_t rows, int cols_p, void *dst, int cols, int es,
+                        hipStream_t s);
 // backward
 hipError_t launch_bwd_route(const Plan &p, hipStream_t s);      // idx -> counts, permutation
 hipError_t launch_bwd_gather(const Plan &p, hipStream_t s);     // x and gate*dout rows, permuted
