@@ -630,7 +630,12 @@ __device__ __forceinline__ void gemm_tile8(const GemmArgs &g, const TileLoc &t,
 // barriers instead of 10.  On a compute-bound dense GEMM this structure ran
 // at 0.51 of the bf16 MFMA peak against 0.40 for the 160-row one.  The hot
 // experts' weights are read by many chunks, so they keep the default cache
-// policy.
+// policy.  A chunk of at most 128 rows (an expert's last, partial chunk) is
+// a narrow tile (kNarrow): wave w computes 64 weight rows (w % 4: row
+// quarter; for GATE_UP the gate and up rows of its 32 features) x 64 tokens
+// (w / 4: token half), so every SIMD does half the full tile's MFMAs instead
+// of two SIMDs idling on empty token quarters.  Loads, LDS layout and each
+// output element's MFMA sequence are the full tile's: bit-identical results.
 constexpr int kHotKS = 32;         // bf16 elements per K-step
 constexpr int kHotOpB = 256 * 64;  // one operand's stage: 256 rows x 64 bytes
 
@@ -640,15 +645,17 @@ constexpr int kHotOpB = 256 * 64;  // one operand's stage: 256 rows x 64 bytes
 // granules (row * 4 + chunk) mod 16 are all distinct: no bank conflicts.
 __device__ __forceinline__ int hot_swz(int row) { return (row >> 2) & 3; }
 
-template <int MODE>
+template <int MODE, bool kNarrow>
 __device__ __forceinline__ void gemm_hot_tile(const GemmArgs &g, const TileLoc &t,
                                               char *const (&s_w)[3], char *const (&tl)[3]) {
   constexpr uint32_t ES = 2;
   constexpr bool kGateUp = MODE == MODE_GATE_UP;
+  constexpr int NA = kNarrow ? 2 : 4;  // 32-row weight blocks per wave
   const int e = t.e, rb = t.rb, m0 = t.m0, mcount = t.mcount;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int wr = wave >> 2, wc = wave & 3;
+  // full: row half wr, token quarter wc; narrow: row quarter wr, token half wc
+  const int wr = kNarrow ? wave & 3 : wave >> 2, wc = kNarrow ? wave >> 2 : wave & 3;
   const int r = lane & 31, h = lane >> 5;
   const int K = g.K;
   const uint32_t rowb = static_cast<uint32_t>(K) * ES;
@@ -712,13 +719,17 @@ __device__ __forceinline__ void gemm_hot_tile(const GemmArgs &g, const TileLoc &
 
   // Fragment byte offsets within a stage, per 16-element piece q: lane
   // (r, h) reads logical chunk 2q + h of its rows.
-  int aoff[2][4], boff[2][2];
+  int aoff[2][NA], boff[2][2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = kGateUp ? (i < 2 ? wr * 64 + i * 32 + r : 128 + wr * 64 + (i - 2) * 32 + r)
-                              : wr * 128 + i * 32 + r;
+    for (int i = 0; i < NA; ++i) {
+      int row;
+      if (kNarrow)  // GATE_UP: block 0 gate rows, block 1 up rows of features wr*32 + [0, 32)
+        row = kGateUp ? i * 128 + wr * 32 + r : wr * 64 + i * 32 + r;
+      else
+        row = kGateUp ? (i < 2 ? wr * 64 + i * 32 + r : 128 + wr * 64 + (i - 2) * 32 + r)
+                      : wr * 128 + i * 32 + r;
       aoff[q][i] = row * 64 + (((2 * q + h) ^ hot_swz(row)) << 4);
     }
 #pragma unroll
@@ -727,9 +738,9 @@ __device__ __forceinline__ void gemm_hot_tile(const GemmArgs &g, const TileLoc &
       boff[q][j] = kHotOpB + row * 64 + (((2 * q + h) ^ hot_swz(row)) << 4);
     }
   }
-  floatx16 acc[4][2];
+  floatx16 acc[NA][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NA; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -737,13 +748,13 @@ __device__ __forceinline__ void gemm_hot_tile(const GemmArgs &g, const TileLoc &
   auto compute = [&](const char *stage) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      uint4 fa[4], fb[2];
+      uint4 fa[NA], fb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const uint4 *>(stage + aoff[q][i]);
+      for (int i = 0; i < NA; ++i) fa[i] = *reinterpret_cast<const uint4 *>(stage + aoff[q][i]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const uint4 *>(stage + boff[q][j]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NA; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) MfmaOps<bf16_t>::piece(acc[i][j], fa[i], fb[j]);
     }
@@ -791,7 +802,11 @@ __device__ __forceinline__ void gemm_hot_tile(const GemmArgs &g, const TileLoc &
   ts.m0 = m0 + wc * 64;
   ts.mcount = max(0, min(mcount - wc * 64, 64));
   (void)tl;
-  if (kGateUp) {
+  if constexpr (kNarrow) {  // features rb*128 + wr*32 (GATE_UP) / rows rb*256 + wr*64 (DOWN)
+    const floatx16 pr[2][2] = {{acc[0][0], acc[0][1]}, {acc[1][0], acc[1][1]}};
+    stage_epilogue<MODE, 2>(g.out, nullptr, g.out_ld, g.nrows, ts, pr, st,
+                            kGateUp ? rb * 128 + wr * 32 : rb * 256 + wr * 64, r, h, lane);
+  } else if (kGateUp) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {  // features rb*128 + wr*64 + 32p + [0, 32): gate block p, up p + 2
       const floatx16 pr[2][2] = {{acc[p][0], acc[p][1]}, {acc[p + 2][0], acc[p + 2][1]}};
@@ -826,7 +841,8 @@ __global__ void __launch_bounds__(kThreads8) gemm8w_kernel(GemmArgs g) {
   char *const tl[3] = {s_t0, s_t1, s_t2};
   if constexpr (MODE == MODE_GATE_UP || MODE == MODE_DOWN) {
     if (t.mt == kHotMT) {
-      gemm_hot_tile<MODE>(g, t, s_w, tl);
+      if (t.mcount <= 128) gemm_hot_tile<MODE, true>(g, t, s_w, tl);
+      else gemm_hot_tile<MODE, false>(g, t, s_w, tl);
       return;
     }
   }
