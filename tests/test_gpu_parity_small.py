@@ -203,6 +203,15 @@ def test_routing_and_outputs_fuzz():
     assert seen_k_eq_e
 
 
+@pytest.mark.parametrize("k", [4, 5, 8, 9, 12, 13, 16, 17, 33])
+def test_combine_every_batch_size(k):
+    """The combine loads each token's slots in batches whose size it picks
+    from k (4, 8, 12 or 16): every size, one slot past it, and several
+    batches (k = 33), bf16 and all elements against the oracle."""
+    cfg = synth.Config(f"k{k}", T=40, d=128, I=64, N=24, Z=16, k=k, dtype="bf16", seed=200 + k)
+    full_check(cfg, synth.host_inputs(cfg), poison=True)
+
+
 def test_deterministic_bitwise():
     cfg = RAGGED[1]
     inp = synth.host_inputs(cfg)
