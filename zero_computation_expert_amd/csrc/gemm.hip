@@ -48,7 +48,8 @@
 //   * For 160-token chunks (bf16) the workgroup has 8 waves, two per SIMD
 //     (gemm8w_kernel), and experts of more than 160 rows run 256 x 256
 //     hot-expert tiles (gemm_hot_tile), which do more MFMA work per loaded
-//     and per LDS-read byte.
+//     and per LDS-read byte (a last chunk of at most 128 rows as a narrow
+//     tile: the waves split weight rows four ways and tokens two ways).
 #include "gemm_common.h"
 
 namespace moezc {
