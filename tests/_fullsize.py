@@ -10,7 +10,7 @@ are pinned bit-identical to the token-major oracle forward.
 
 Which tokens: all of them where that is cheap, otherwise a cover of every
 32-row block of every expert's permuted rows.  The expert GEMMs work on
-chunks of 32, 128 or 160 permuted rows (all multiples of 32), and one token
+chunks of 32, 128, 160 or 256 permuted rows (all multiples of 32), and one token
 row's output passes through every weight row block of both projections of
 its chunk, so a token in every 32-row block means every (expert, row block,
 chunk, 32-token block) tile of both expert GEMMs has an output compared,
