@@ -328,6 +328,27 @@ def test_empty_and_single_token():
     assert out.shape == (0, cfg.d) and (c.cpu() == 0).all()
 
 
+def test_widths_not_multiples_of_8_timed_and_untimed_agree():
+    """The zero-padded path under the stage timer (its copies run outside
+    the timed stages): every stage recorded, outputs bit-identical to the
+    untimed call."""
+    cfg = ODD[0]
+    inp = synth.host_inputs(cfg)
+    dev = "cuda:0"
+    t = lambda a: torch.from_numpy(a).view(torch.bfloat16).to(dev)  # noqa: E731
+    args = (t(inp["x"]), t(inp["W_router"]), torch.from_numpy(inp["bias"]).to(dev),
+            t(inp["W_gate"]), t(inp["W_up"]), t(inp["W_down"]), cfg.N, cfg.Z, cfg.k)
+    ref = moe.forward(*args)
+    timer = moe.Timer(2)
+    got = moe.forward(*args, timer=timer)
+    n, ms = timer.read()
+    timer.close()
+    assert n == 1 and all(v > 0 for v in ms.values()), ms
+    for u, v in zip(ref, got):
+        assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.int16) if v.dtype == torch.bfloat16 else v)
+
+
 def test_stage_timer_records_every_stage():
     cfg = RAGGED[1]
     inp = synth.host_inputs(cfg)
