@@ -43,8 +43,12 @@ __device__ __forceinline__ void top2_below(const uint64_t (&key)[VPL], uint64_t 
 // marks an absent expert (every real key is > 0).
 // The block (kTokPerBlk waves) covers kTokPerBlk consecutive tokens and
 // writes its per-expert selection histogram to blockhist[blockIdx.x].
-template <int VPL>
-__global__ void __launch_bounds__(kTokPerBlk * kWave) topk_kernel(const float *__restrict__ logits,
+// kSplit: the logits arrive as K-slice partials to add.  Without that sum's
+// registers, and with at most 768 experts, a block fits twice per CU (the
+// second launch bound asks for 8 waves per SIMD; wider keys would spill).
+template <int VPL, bool kSplit>
+__global__ void __launch_bounds__(kTokPerBlk * kWave, (kSplit || VPL > 12) ? 1 : 8)
+    topk_kernel(const float *__restrict__ logits,
                                                    int split, int64_t part_stride,
                                                    const float *__restrict__ bias, int64_t T,
                                                    int E, int k, int32_t *__restrict__ idx_out,
@@ -77,7 +81,8 @@ __global__ void __launch_bounds__(kTokPerBlk * kWave) topk_kernel(const float *_
     // widest expert counts, whose registers are already full).
     constexpr int U = VPL <= 16 ? 4 : 1;
     int sl = 1;
-    for (; sl + U <= split; sl += U) {
+    if (!kSplit) sl = split;  // one slice (the launch guarantees split == 1)
+    for (; kSplit && sl + U <= split; sl += U) {
       float a[U][VPL];
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -91,7 +96,7 @@ __global__ void __launch_bounds__(kTokPerBlk * kWave) topk_kernel(const float *_
 #pragma unroll
         for (int s = 0; s < VPL; ++s) l[s] += a[u][s];
     }
-    for (; sl < split; ++sl) {
+    for (; kSplit && sl < split; ++sl) {
 #pragma unroll
       for (int s = 0; s < VPL; ++s) {
         int e = s * kWave + lane;
@@ -348,6 +353,23 @@ static bool sum_slices_first(const Plan &p) {
   return p.rs.split > 1 && p.nblk < 128 && bytes >= (int64_t(1) << 19);
 }
 
+template <bool kSplit>
+static void launch_topk_v(const Plan &p, int vpl, int split, int64_t n, hipStream_t s) {
+  const dim3 grid(p.nblk), block(kTokPerBlk * kWave);
+  if (vpl <= 4)
+    hipLaunchKernelGGL((topk_kernel<4, kSplit>), grid, block, 0, s, p.logits, split, n, p.bias,
+                       p.T, p.E, p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
+  else if (vpl <= 12)  // up to 768 experts
+    hipLaunchKernelGGL((topk_kernel<12, kSplit>), grid, block, 0, s, p.logits, split, n, p.bias,
+                       p.T, p.E, p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
+  else if (vpl <= 16)
+    hipLaunchKernelGGL((topk_kernel<16, kSplit>), grid, block, 0, s, p.logits, split, n, p.bias,
+                       p.T, p.E, p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
+  else
+    hipLaunchKernelGGL((topk_kernel<32, kSplit>), grid, block, 0, s, p.logits, split, n, p.bias,
+                       p.T, p.E, p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
+}
+
 hipError_t launch_topk(const Plan &p, hipStream_t s) {
   int split = p.rs.split;
   const int64_t n = p.T * p.E;
@@ -362,20 +384,9 @@ hipError_t launch_topk(const Plan &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     split = 1;
   }
-  dim3 grid(p.nblk), block(kTokPerBlk * kWave);
-  int vpl = (p.E + kWave - 1) / kWave;
-  if (vpl <= 4)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p.logits, split, n, p.bias, p.T, p.E,
-                       p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
-  else if (vpl <= 12)  // up to 768 experts
-    hipLaunchKernelGGL(topk_kernel<12>, grid, block, 0, s, p.logits, split, n, p.bias, p.T, p.E,
-                       p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
-  else if (vpl <= 16)
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p.logits, split, n, p.bias, p.T, p.E,
-                       p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
-  else
-    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p.logits, split, n, p.bias, p.T, p.E,
-                       p.k, p.idx, p.gate, p.blockhist, p.routed_scale);
+  const int vpl = (p.E + kWave - 1) / kWave;
+  if (split > 1) launch_topk_v<true>(p, vpl, split, n, s);
+  else launch_topk_v<false>(p, vpl, split, n, s);
   return hipGetLastError();
 }
 
