@@ -4,6 +4,7 @@ captured by a caller that preallocates its buffers (serving loops with few
 tokens are launch-bound).  Each captured call is replayed several times,
 with eager work (clearing the outputs) and synchronisations between the
 replays, and every replay must give bit for bit the eager call's outputs."""
+import numpy as np
 import pytest
 
 import synth
@@ -35,7 +36,20 @@ def capture(fn):
 @pytest.mark.parametrize("wl", ["tiny", "small"])
 def test_forward_graph_replays_match_eager(wl):
     cfg = synth.CONFIGS[wl]
-    inp = synth.device_inputs(cfg, DEV)
+    check_forward_graph(cfg, synth.device_inputs(cfg, DEV))
+
+
+def test_forward_graph_replays_match_eager_widths_not_multiples_of_8():
+    """The zero-padded path (its copy kernels are captured with the rest)."""
+    cfg = synth.Config("odd_graph", T=77, d=100, I=36, N=6, Z=3, k=3, dtype="bf16", seed=16)
+    h = synth.host_inputs(cfg)
+    inp = {n: (torch.from_numpy(v).view(torch.bfloat16) if v.dtype == np.uint16
+               else torch.from_numpy(v)).to(DEV) for n, v in h.items()}
+    check_forward_graph(cfg, inp)
+
+
+def check_forward_graph(cfg, inp):
+    wl = cfg.name
     args = (inp["x"], inp["W_router"], inp["bias"], inp["W_gate"], inp["W_up"], inp["W_down"],
             cfg.N, cfg.Z, cfg.k)
     T, E, k = cfg.T, cfg.E, cfg.k
